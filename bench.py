@@ -1,0 +1,191 @@
+"""Throughput of the chunked SSD scan on one MI355X, as one JSON line.
+
+A step is one ssd_chunk_scan_fwd call (all four kernels: chunk_cumsum, chunk_state,
+state_pass, chunk_scan) over the whole batch of the 128K-token workload
+(long_context_b1_L131072_h48: batch 1, L 131072, H 48, P 64, N 128, Q 256, bf16), with
+every input already resident in HBM.  W untimed warm-up steps, then exactly K timed
+steps between two device synchronisations.
+
+Besides the headline tokens/s the line carries:
+  roofline      the dominant kernel's achieved HBM rate (algorithmic bytes per launch /
+                its mean duration, from HIP events around each launch on the stream it
+                runs on) against the 8 TB/s peak;
+  kernels       the same figures for all four kernels, plus matrix-core rates;
+  end_to_end    the method's bytes / step time against peak HBM bandwidth;
+  cpu_baseline  the fp64 CPU oracle timed on this host's cores on the same inputs.
+
+Algorithmic bytes count every input a kernel needs once and every output it must write
+once, in the dtype the library stores it in (activations bf16, decays and local states
+float32, states entering a chunk bf16).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 128K-token layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-steps", type=int, default=0, help="launches per kernel for per-kernel timing "
+                    "(default: --steps)")
+    return ap.parse_args()
+
+
+def alg_bytes(w):
+    """Algorithmic bytes per launch of each kernel and of the whole method."""
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    e = w.act_bytes
+    nc = w.nchunks
+    cum_e = 8 if w.dtype == "f32" else 4
+    x = b * L * H * P * e
+    y = x
+    dt = b * L * H * e
+    bc = b * L * G * N * e                      # one of B or C
+    cum = b * H * nc * Q * cum_e
+    states = b * nc * H * P * N
+    init = final = b * H * P * N * 4
+    k = {
+        "chunk_cumsum": dt + cum,
+        "chunk_state": x + bc + cum + states * 4,
+        "state_pass": states * 4 + states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
+        "chunk_scan": x + 2 * bc + cum + states * e + y,
+    }
+    method = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final + 2 * states * 4 + 2 * states * e
+    return k, method
+
+
+def alg_flops(w):
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nc = w.nchunks
+    per_chunk_state = H * 2 * Q * N * P
+    per_chunk_scan = H * (Q * (Q + 1) * P + 2 * Q * N * P) + G * Q * (Q + 1) * N
+    return {"chunk_state": b * nc * per_chunk_state, "chunk_scan": b * nc * per_chunk_scan}
+
+
+def cpu_baseline(d, w):
+    """The fp64 oracle (plain C, one thread per (batch, head) pair) on this host."""
+    import numpy as np
+    import oracle
+    x, dt, A, B, C, D = (oracle.to_f64(d[k]) for k in ("x", "dt", "A", "B", "C", "D"))
+    init = None if d.get("init_state") is None else oracle.to_f64(d["init_state"])
+    threads = min(oracle.default_threads(), w.batch * w.nheads)
+    t0 = time.perf_counter()
+    oracle.seq(x, dt, A, B, C, D, init, nthreads=threads)
+    dt_s = time.perf_counter() - t0
+    del x
+    return {"value": w.tokens / dt_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt_s, 3),
+            "sample": "the whole workload (%d x %d tokens, %d heads), fp64 sequential recurrence, "
+                      "one thread per (batch, head) pair" % (w.batch, w.seqlen, w.nheads)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this library is a single-GPU kernel set; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from chunked_linear_recurrence_amd import inputs, ssd, WORKLOADS, BENCH_WORKLOAD
+
+    w = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    if w.layers > 1:
+        print("bench.py times single-layer workloads", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ssd.lib()
+    print("[bench] generating %s" % w.name, file=sys.stderr, flush=True)
+    d = inputs.make(w)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in d.items()}
+    dims = ssd.dims_of(g["x"], g["B"])
+    ws = ssd.alloc_workspace(ssd.workspace_bytes(dims, w.chunk), dev)
+    y = torch.empty_like(g["x"])
+    fin = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(first=1, last=4):
+        ssd.fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["init_state"], w.chunk, y=y,
+                final_state=fin, workspace=ws, stream=stream, first_stage=first, last_stage=last)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    tokens_per_s = w.tokens / (ms_step * 1e-3)
+
+    # per-kernel durations: HIP events around each single-kernel launch on the same stream
+    names = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_scan"]
+    kb, method_bytes = alg_bytes(w)
+    kf = alg_flops(w)
+    ksteps = args.kernel_steps or args.steps
+    kernels = {}
+    for stage, name in enumerate(names, start=1):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(ksteps)]
+        for a, b_ in evs:
+            a.record(stream)
+            step(stage, stage)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b_) for a, b_ in evs) / ksteps * 1e3
+        gbs = kb[name] / (us * 1e-6) / 1e9
+        rec = {"us": round(us, 2), "alg_bytes": kb[name], "GB_s": round(gbs, 1),
+               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if name in kf:
+            tf = kf[name] / (us * 1e-6) / 1e12
+            rec.update({"alg_flops": kf[name], "TFLOP_s": round(tf, 2),
+                        "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+        kernels[name] = rec
+    torch.cuda.synchronize()
+    dom = max(names, key=lambda n: kernels[n]["us"])
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB_s"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": kernels[dom]["hbm_frac"], "traffic": None,
+            "alg_bytes_per_launch": kb[dom], "mean_launch_us": kernels[dom]["us"]}
+    e2e_gbs = method_bytes / (ms_step * 1e-3) / 1e9
+
+    out = {
+        "metric": "SSD chunked-scan tokens/s per GPU; % of bf16 MFMA peak and % of HBM BW",
+        "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk": w.chunk},
+        "roofline": roof,
+        "end_to_end": {"method_bytes": method_bytes, "GB_s": round(e2e_gbs, 1),
+                       "hbm_frac": round(e2e_gbs / HBM_PEAK_GBS, 4)},
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(d, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

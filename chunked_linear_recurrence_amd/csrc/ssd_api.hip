@@ -1,0 +1,385 @@
+// C-ABI entry points of libssdscan: argument checks, workspace carving and the launch
+// sequence chunk_cumsum -> chunk_state -> state_pass -> chunk_scan on the caller's
+// stream.  Nothing here allocates device memory or waits on the device.
+//
+// Steps follow the page "分块推理：解锁循环模型并行计算，实现长序列高效处理":
+// [分块推理 §2.1] (intra-chunk parts from a zero state), [分块推理 §2.2] (state pass and
+// the by_inter correction) and, for the layer stack, [分块推理 §3.2] (vertical segments
+// with a per-layer state store).
+#include "../../include/libssdscan.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "ssd_common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ssd_status_t fail(ssd_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+ssd_status_t ok() {
+    g_err.clear();
+    return SSD_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t dA, bintra, bin, total;
+};
+
+int64_t act_bytes(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t lim, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > lim / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Workspace of one layer call over `L` tokens.
+bool layout_for(const ssd_dims_t &d, int64_t L, int32_t Q, Layout *lo) {
+    const int64_t lim = INT64_C(1) << 60;
+    const int64_t nc = (L + Q - 1) / Q;
+    int64_t bhn, states, t;
+    if (!mul_ok(d.batch, d.nheads, lim, &bhn) || !mul_ok(bhn, nc, lim, &bhn)) return false;
+    if (!mul_ok(d.headdim, d.dstate, lim, &states) || !mul_ok(states, bhn, lim, &states)) return false;
+    if (!mul_ok(bhn, Q, lim, &t)) return false;
+    size_t off = 0;
+    lo->dA = off;
+    off += align_up((size_t)t * (d.dtype == SSD_F32 ? 8 : 4));
+    lo->bintra = off;
+    off += align_up((size_t)states * 4);
+    lo->bin = off;
+    off += align_up((size_t)states * act_bytes(d.dtype));
+    lo->total = off;
+    return true;
+}
+
+ssd_status_t check_dims(const ssd_dims_t *d, int32_t Q) {
+    if (!d) return fail(SSD_ERR_NULL_ARG, "dims is NULL");
+    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16)
+        return fail(SSD_ERR_BAD_DTYPE, "dtype %d is not SSD_F32 (0) or SSD_BF16 (1)", d->dtype);
+    if (d->reserved != 0) return fail(SSD_ERR_BAD_SHAPE, "dims.reserved must be 0");
+    if (d->batch <= 0 || d->seqlen <= 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 ||
+        d->ngroups <= 0)
+        return fail(SSD_ERR_BAD_SHAPE, "every dimension must be >= 1 (batch %lld seqlen %lld nheads %lld "
+                    "headdim %lld dstate %lld ngroups %lld)", (long long)d->batch, (long long)d->seqlen,
+                    (long long)d->nheads, (long long)d->headdim, (long long)d->dstate, (long long)d->ngroups);
+    if (d->nheads % d->ngroups != 0)
+        return fail(SSD_ERR_BAD_SHAPE, "nheads %lld is not a multiple of ngroups %lld",
+                    (long long)d->nheads, (long long)d->ngroups);
+    if (Q <= 0) return fail(SSD_ERR_BAD_SHAPE, "chunk_Q must be >= 1 (got %d)", Q);
+    if (d->seqlen > INT32_MAX || d->nheads > 65536 || d->batch > 65536 ||
+        d->nheads * d->headdim > INT32_MAX / 16)
+        return fail(SSD_ERR_UNSUPPORTED, "dimensions exceed the 32-bit index range of the kernels");
+    if (!ssd_shape_supported(d->dtype, Q, d->headdim, d->dstate))
+        return fail(SSD_ERR_UNSUPPORTED, "no compiled kernel for dtype %d chunk_Q %d headdim %lld dstate %lld",
+                    d->dtype, Q, (long long)d->headdim, (long long)d->dstate);
+    const int64_t nc = (d->seqlen + Q - 1) / Q;
+    if (d->batch * nc * d->nheads > INT32_MAX)
+        return fail(SSD_ERR_UNSUPPORTED, "batch * chunks * heads exceeds the grid range");
+    return SSD_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Tensors read or written with 16-byte vector accesses must be 16-byte aligned; A and D
+// (scalar float loads) need 4 bytes, dt its element size.
+ssd_status_t check_alignment(const void *x, const void *dt, const void *A, const void *B, const void *C,
+                             const void *D, const void *init, const void *y, const void *fin,
+                             const void *ws, int32_t dtype) {
+    const void *vec[] = {x, B, C, init, y, fin, ws};
+    for (const void *q : vec)
+        if (q && !aligned16(q)) return fail(SSD_ERR_MISALIGNED, "pointer %p is not 16-byte aligned", q);
+    const uintptr_t dtal = dtype == SSD_BF16 ? 2 : 4;
+    if (((uintptr_t)dt & (dtal - 1)) || ((uintptr_t)A & 3u) || (D && ((uintptr_t)D & 3u)))
+        return fail(SSD_ERR_MISALIGNED, "dt, A or D is not aligned to its element size");
+    return SSD_OK;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Work partition: heads per workgroup so that there are at least `target` workgroups
+// (when the problem has that many heads to spread).  Only the split changes, never the
+// arithmetic of any output element.
+int heads_per_wg(int64_t units, int64_t hpg, int64_t target, const char *env) {
+    if (const char *s = getenv(env)) {
+        const int v = atoi(s);
+        if (v >= 1) return (int)(v < hpg ? v : hpg);
+    }
+    int64_t hg = hpg * units / target;
+    if (hg < 1) hg = 1;
+    if (hg > hpg) hg = hpg;
+    return (int)hg;
+}
+
+ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q) {
+    ssd::Problem p;
+    memset(&p, 0, sizeof(p));
+    p.batch = (int)d.batch;
+    p.L = (int)L;
+    p.H = (int)d.nheads;
+    p.P = (int)d.headdim;
+    p.N = (int)d.dstate;
+    p.G = (int)d.ngroups;
+    p.Q = Q;
+    p.nc = (int)((L + Q - 1) / Q);
+    p.dtype = d.dtype;
+    const int64_t units = d.batch * p.nc * d.ngroups;
+    const int64_t hpg = d.nheads / d.ngroups;
+    p.heads_per_wg_state = heads_per_wg(units, hpg, 1024, "SSD_HEADS_PER_WG_STATE");
+    p.heads_per_wg_scan = heads_per_wg(units, hpg, 2048, "SSD_HEADS_PER_WG_SCAN");
+    return p;
+}
+
+ssd_status_t run_layer(const ssd::Problem &p, hipStream_t s, int first_stage, int last_stage) {
+    hipError_t e = hipSuccess;
+    auto in = [&](int k) { return first_stage <= k && k <= last_stage; };
+    if (in(1) && (e = ssd::launch_chunk_cumsum(p, s)) != hipSuccess)
+        return fail(SSD_ERR_HIP, "chunk_cumsum launch failed: %s", hipGetErrorString(e));
+    if (in(2) && (e = ssd::launch_chunk_state(p, s)) != hipSuccess)
+        return fail(SSD_ERR_HIP, "chunk_state launch failed: %s", hipGetErrorString(e));
+    if (in(3) && (e = ssd::launch_state_pass(p, s)) != hipSuccess)
+        return fail(SSD_ERR_HIP, "state_pass launch failed: %s", hipGetErrorString(e));
+    if (in(4) && (e = ssd::launch_chunk_scan(p, s)) != hipSuccess)
+        return fail(SSD_ERR_HIP, "chunk_scan launch failed: %s", hipGetErrorString(e));
+    return SSD_OK;
+}
+
+ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, const float *A,
+                      const void *B, const void *C, const float *D, const float *init_state,
+                      int32_t chunk_Q, void *y, float *final_state, uint32_t flags, void *workspace,
+                      size_t workspace_bytes, void *stream, int first_stage, int last_stage) {
+    ssd_status_t st = check_dims(dims, chunk_Q);
+    if (st != SSD_OK) return st;
+    const ssd_dims_t &d = *dims;
+    if (!x || !dt || !A || !B || !C || !y)
+        return fail(SSD_ERR_NULL_ARG, "x, dt, A, B, C and y must be non-NULL");
+    if (flags & ~SSD_FLAG_RESIDUAL) return fail(SSD_ERR_BAD_SHAPE, "unknown flag bits 0x%x", flags);
+    if (st = check_alignment(x, dt, A, B, C, D, init_state, y, final_state, workspace, d.dtype); st != SSD_OK)
+        return st;
+    Layout lo;
+    if (!layout_for(d, d.seqlen, chunk_Q, &lo)) return fail(SSD_ERR_BAD_SHAPE, "sizes overflow");
+    if (!workspace || workspace_bytes < lo.total)
+        return fail(SSD_ERR_WORKSPACE, "workspace %p of %zu bytes; %zu bytes are needed", workspace,
+                    workspace_bytes, lo.total);
+    const size_t e = (size_t)act_bytes(d.dtype);
+    const size_t nx = (size_t)(d.batch * d.seqlen * d.nheads * d.headdim) * e;
+    const size_t ns = (size_t)(d.batch * d.nheads * d.headdim * d.dstate) * 4;
+    if (overlap(y, nx, x, nx)) return fail(SSD_ERR_ALIAS, "y overlaps x");
+    if (final_state && init_state && final_state != init_state && overlap(final_state, ns, init_state, ns))
+        return fail(SSD_ERR_ALIAS, "final_state partially overlaps init_state");
+    if (overlap(workspace, lo.total, x, nx) || overlap(workspace, lo.total, y, nx))
+        return fail(SSD_ERR_ALIAS, "workspace overlaps x or y");
+    if (final_state && overlap(final_state, ns, y, nx)) return fail(SSD_ERR_ALIAS, "final_state overlaps y");
+
+    ssd::Problem p = make_problem(d, d.seqlen, chunk_Q);
+    p.x = x;
+    p.x_bs = d.seqlen * d.nheads * d.headdim;
+    p.y = y;
+    p.y_bs = p.x_bs;
+    p.dt = dt;
+    p.dt_bs = d.seqlen * d.nheads;
+    p.B = B;
+    p.C = C;
+    p.bc_bs = d.seqlen * d.ngroups * d.dstate;
+    p.A = A;
+    p.D = D;
+    p.init = init_state;
+    p.final_state = final_state;
+    p.flags = flags;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    p.dA_cum = ws + lo.dA;
+    p.b_intra = reinterpret_cast<float *>(ws + lo.bintra);
+    p.b_in = ws + lo.bin;
+    st = run_layer(p, static_cast<hipStream_t>(stream), first_stage, last_stage);
+    return st == SSD_OK ? ok() : st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ssd_shape_supported(int32_t dtype, int32_t chunk_Q, int64_t headdim, int64_t dstate) {
+    if (dtype != SSD_F32 && dtype != SSD_BF16) return 0;
+    if (headdim > 1024 || dstate > 1024) return 0;
+    const int P = (int)headdim, N = (int)dstate;
+    return ssd::chunk_state_supported(dtype, chunk_Q, P, N) && ssd::chunk_scan_supported(dtype, chunk_Q, P, N);
+}
+
+size_t ssd_chunk_scan_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q) {
+    if (check_dims(dims, chunk_Q) != SSD_OK) return 0;
+    Layout lo;
+    if (!layout_for(*dims, dims->seqlen, chunk_Q, &lo)) return 0;
+    return lo.total;
+}
+
+ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, const void *x, const void *dt, const float *A,
+                                const void *B, const void *C, const float *D, const float *init_state,
+                                int32_t chunk_Q, void *y, float *final_state, uint32_t flags,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    return fwd_impl(dims, x, dt, A, B, C, D, init_state, chunk_Q, y, final_state, flags, workspace,
+                    workspace_bytes, stream, 1, 4);
+}
+
+ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const void *dt, const float *A,
+                                   const void *B, const void *C, const float *D, const float *init_state,
+                                   int32_t chunk_Q, void *y, float *final_state, uint32_t flags,
+                                   void *workspace, size_t workspace_bytes, void *stream,
+                                   int32_t first_stage, int32_t last_stage) {
+    if (first_stage < 1 || last_stage > 4 || first_stage > last_stage)
+        return fail(SSD_ERR_BAD_SHAPE, "stages must satisfy 1 <= first_stage <= last_stage <= 4");
+    return fwd_impl(dims, x, dt, A, B, C, D, init_state, chunk_Q, y, final_state, flags, workspace,
+                    workspace_bytes, stream, first_stage, last_stage);
+}
+
+ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_t offsets[4]) {
+    ssd_status_t st = check_dims(dims, chunk_Q);
+    if (st != SSD_OK) return st;
+    if (!offsets) return fail(SSD_ERR_NULL_ARG, "offsets is NULL");
+    Layout lo;
+    if (!layout_for(*dims, dims->seqlen, chunk_Q, &lo)) return fail(SSD_ERR_BAD_SHAPE, "sizes overflow");
+    offsets[0] = lo.dA;
+    offsets[1] = lo.bintra;
+    offsets[2] = lo.bin;
+    offsets[3] = lo.total;
+    return ok();
+}
+
+// Segmented (vertical) stack: workspace = two activation buffers of one segment + one
+// layer's workspace over one segment.
+static bool seg_layout(const ssd_dims_t &d, int32_t Q, int64_t V, size_t *act_off, size_t *act_bytes_each,
+                       size_t *layer_off, size_t *total) {
+    const int64_t Vs = V < d.seqlen ? V : d.seqlen;
+    Layout lo;
+    if (!layout_for(d, Vs, Q, &lo)) return false;
+    const size_t a = align_up((size_t)(d.batch * Vs * d.nheads * d.headdim) * (size_t)act_bytes(d.dtype));
+    *act_off = 0;
+    *act_bytes_each = a;
+    *layer_off = 2 * a;
+    *total = 2 * a + lo.total;
+    return true;
+}
+
+size_t ssd_segmented_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q, int64_t V) {
+    if (check_dims(dims, chunk_Q) != SSD_OK || V < 1) return 0;
+    size_t a, ae, l, t;
+    if (!seg_layout(*dims, chunk_Q, V, &a, &ae, &l, &t)) return 0;
+    return t;
+}
+
+ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, int64_t V, const void *x0,
+                                      const void *dt, const float *A, const void *B, const void *C,
+                                      const float *D, float *layer_states, int32_t chunk_Q, uint32_t flags,
+                                      void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    ssd_status_t st = check_dims(dims, chunk_Q);
+    if (st != SSD_OK) return st;
+    const ssd_dims_t &d = *dims;
+    if (n_layers < 1) return fail(SSD_ERR_BAD_SHAPE, "n_layers must be >= 1 (got %d)", n_layers);
+    if (V < 1) return fail(SSD_ERR_BAD_SHAPE, "V must be >= 1 (got %lld)", (long long)V);
+    if (!x0 || !dt || !A || !B || !C || !layer_states || !y)
+        return fail(SSD_ERR_NULL_ARG, "x0, dt, A, B, C, layer_states and y must be non-NULL");
+    if (flags & ~SSD_FLAG_RESIDUAL) return fail(SSD_ERR_BAD_SHAPE, "unknown flag bits 0x%x", flags);
+    if (st = check_alignment(x0, dt, A, B, C, D, layer_states, y, layer_states, workspace, d.dtype); st != SSD_OK)
+        return st;
+    size_t act_off, act_each, layer_off, total;
+    if (!seg_layout(d, chunk_Q, V, &act_off, &act_each, &layer_off, &total))
+        return fail(SSD_ERR_BAD_SHAPE, "sizes overflow");
+    if (!workspace || workspace_bytes < total)
+        return fail(SSD_ERR_WORKSPACE, "workspace %p of %zu bytes; %zu bytes are needed", workspace,
+                    workspace_bytes, total);
+    const size_t e = (size_t)act_bytes(d.dtype);
+    const size_t nx = (size_t)(d.batch * d.seqlen * d.nheads * d.headdim) * e;
+    const size_t ns = (size_t)n_layers * (size_t)(d.batch * d.nheads * d.headdim * d.dstate) * 4;
+    if (overlap(y, nx, x0, nx)) return fail(SSD_ERR_ALIAS, "y overlaps x0");
+    if (overlap(workspace, total, x0, nx) || overlap(workspace, total, y, nx) ||
+        overlap(workspace, total, layer_states, ns) || overlap(layer_states, ns, y, nx))
+        return fail(SSD_ERR_ALIAS, "workspace, layer_states and y must not overlap each other or x0");
+
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    void *act[2] = {ws + act_off, ws + act_off + act_each};
+    const int64_t Vs = V < d.seqlen ? V : d.seqlen;
+    Layout lo;
+    layout_for(d, Vs, chunk_Q, &lo);
+    unsigned char *lws = ws + layer_off;
+    const int64_t HP = d.nheads * d.headdim, GN = d.ngroups * d.dstate;
+    const int64_t state_elems = d.batch * d.nheads * d.headdim * d.dstate;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    for (int64_t s0 = 0; s0 < d.seqlen; s0 += V) {
+        const int64_t len = (d.seqlen - s0) < V ? (d.seqlen - s0) : V;
+        for (int l = 0; l < n_layers; ++l) {
+            ssd::Problem p = make_problem(d, len, chunk_Q);
+            if (l == 0) {
+                p.x = static_cast<const unsigned char *>(x0) + (size_t)(s0 * HP) * e;
+                p.x_bs = d.seqlen * HP;
+            } else {
+                p.x = act[(l - 1) & 1];
+                p.x_bs = Vs * HP;
+            }
+            if (l == n_layers - 1) {
+                p.y = static_cast<unsigned char *>(y) + (size_t)(s0 * HP) * e;
+                p.y_bs = d.seqlen * HP;
+            } else {
+                p.y = act[l & 1];
+                p.y_bs = Vs * HP;
+            }
+            p.dt = static_cast<const unsigned char *>(dt) + (size_t)(s0 * d.nheads) * e;
+            p.dt_bs = d.seqlen * d.nheads;
+            p.B = static_cast<const unsigned char *>(B) + (size_t)(s0 * GN) * e;
+            p.C = static_cast<const unsigned char *>(C) + (size_t)(s0 * GN) * e;
+            p.bc_bs = d.seqlen * GN;
+            p.A = A + (size_t)l * d.nheads;
+            p.D = D ? D + (size_t)l * d.nheads : nullptr;
+            p.init = layer_states + (size_t)l * state_elems;
+            p.final_state = layer_states + (size_t)l * state_elems;
+            p.flags = flags;
+            p.dA_cum = lws + lo.dA;
+            p.b_intra = reinterpret_cast<float *>(lws + lo.bintra);
+            p.b_in = lws + lo.bin;
+            st = run_layer(p, s, 1, 4);
+            if (st != SSD_OK) return st;
+        }
+    }
+    return ok();
+}
+
+const char *ssd_status_string(ssd_status_t status) {
+    switch (status) {
+        case SSD_OK: return "SSD_OK";
+        case SSD_ERR_NULL_ARG: return "SSD_ERR_NULL_ARG";
+        case SSD_ERR_BAD_SHAPE: return "SSD_ERR_BAD_SHAPE";
+        case SSD_ERR_BAD_DTYPE: return "SSD_ERR_BAD_DTYPE";
+        case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+        case SSD_ERR_MISALIGNED: return "SSD_ERR_MISALIGNED";
+        case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
+        case SSD_ERR_HIP: return "SSD_ERR_HIP";
+        case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS";
+    }
+    return "SSD_ERR_UNKNOWN";
+}
+
+const char *ssd_last_error_message(void) { return g_err.c_str(); }
+
+int32_t ssd_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Shared definitions of the libssdscan kernels (gfx950 only).
+//
+// Method: the chunked decomposition of the page
+// "分块推理：解锁循环模型并行计算，实现长序列高效处理", §2-§2.2, cited [分块推理 §n].
+//
+// Matrix-core conventions used by every kernel.  All products are built from 16x16
+// output tiles.  For such a tile a lane l (0..63) with row group g = l / 16 holds:
+//   output / accumulator  D[4g + r][l % 16]          r = 0..3   (f32x4)
+//   A operand             A[l % 16][k]  for 4 values of k
+//   B operand             B[k][l % 16]  for the same 4 values of k
+// and one "tile fragment" (TF) is those 4 operand values: for a K-slice of 16 the lane
+// holds k = 4g + e, e = 0..3.  The contraction only needs A and B to agree on which k
+// each (lane group, element) carries, so any consistent assignment is valid; the kernels
+// use k = 4g + e everywhere.  This lets the 4 consecutive output rows a lane holds be fed
+// back as an A operand without moving data between lanes.
+//   bf16: two K=16 slices are fused into one v_mfma_f32_16x16x32_bf16 (8 values/lane).
+//   fp32: one K=16 slice is four v_mfma_f32_16x16x4f32 (value e feeds the e-th one).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+typedef __bf16 bf16;
+
+constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+
+// One layer's arguments, as the kernels see them.  Token t of batch row b of x/y is at
+// x + b * x_bs + t * H * P; dt at dt + b * dt_bs + t * H; B/C at B + b * bc_bs + t * G * N.
+struct Problem {
+    int batch, L, H, P, N, G, Q, nc;
+    int dtype;                 // 0 = f32, 1 = bf16
+    const void *x;  int64_t x_bs;
+    void *y;        int64_t y_bs;
+    const void *dt; int64_t dt_bs;
+    const void *B;  const void *C; int64_t bc_bs;
+    const float *A; const float *D;          // [H]; D may be null
+    const float *init;                       // [batch, H, P, N] or null
+    float *final_state;                      // [batch, H, P, N] or null
+    uint32_t flags;
+    void *dA_cum;      // [batch, H, nc, Q] of CumT<act>
+    float *b_intra;    // [batch, nc, H, P*N] tile order
+    void *b_in;        // [batch, nc, H, P*N] tile order, act dtype
+    int heads_per_wg_state;   // head group of chunk_state
+    int heads_per_wg_scan;    // head group of chunk_scan
+};
+
+hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s);
+hipError_t launch_chunk_state(const Problem &p, hipStream_t s);
+hipError_t launch_state_pass(const Problem &p, hipStream_t s);
+hipError_t launch_chunk_scan(const Problem &p, hipStream_t s);
+bool chunk_state_supported(int dtype, int Q, int P, int N);
+bool chunk_scan_supported(int dtype, int Q, int P, int N);
+
+// ---------------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------------
+// Type of the log-decay prefix sums: float64 for float32 activations (the differences
+// cum_i - cum_j then keep full fp32 accuracy however large |cum| grows within a chunk),
+// float32 for bfloat16 activations.
+template <typename T> struct CumT { typedef float type; };
+template <> struct CumT<float> { typedef double type; };
+
+template <typename T> struct TF;
+template <> struct TF<float> { typedef f32x4 type; };
+template <> struct TF<bf16> { typedef bf16x4 type; };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }  // RNE
+
+// acc += A0 * B0 (+ A1 * B1): one or two K=16 slices.
+__device__ __forceinline__ f32x4 mma_one(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                       __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_pair(bf16x4 a0, bf16x4 b0, bf16x4 a1, bf16x4 b1, f32x4 c) {
+    bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_one(f32x4 a, f32x4 b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+}
+__device__ __forceinline__ f32x4 mma_pair(f32x4 a0, f32x4 b0, f32x4 a1, f32x4 b1, f32x4 c) {
+    return mma_one(a1, b1, mma_one(a0, b0, c));
+}
+
+template <typename V> __device__ __forceinline__ V zero_frag() { V v; for (int i = 0; i < 4; ++i) v[i] = 0; return v; }
+
+template <typename T>
+__device__ __forceinline__ typename TF<T>::type frag_from_f32(f32x4 v) {
+    typename TF<T>::type r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = from_f32<T>(v[i]);
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 frag_to_f32(typename TF<T>::type v) {
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = to_f32(v[i]);
+    return r;
+}
+
+// 16-byte row piece of an activation tile, as raw 32-bit words.
+struct Row16 { uint32_t w[4]; };
+struct Row8 { uint32_t w[2]; };
+
+// Consecutive workgroups go round-robin to the 8 XCDs (each with its own L2).  Remap so
+// that logically adjacent workgroups (which share B/C data) land on the same XCD.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    if ((n & 7) != 0) return bid;
+    const int per = n >> 3;
+    return (bid & 7) * per + (bid >> 3);
+}
+
+}  // namespace ssd

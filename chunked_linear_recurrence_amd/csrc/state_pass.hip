@@ -1,0 +1,97 @@
+// state_pass: the sequential pass of global states across chunks, [分块推理 §2.2] of the
+// page "分块推理：解锁循环模型并行计算，实现长序列高效处理":
+//
+//     b(-1) = init_state (or 0),   b(c) = b_intra(c) + exp(dA_cum[c, last]) * b(c-1)
+//
+// It writes b_in[c] = b(c-1), the state entering chunk c (in the activation dtype, which
+// is what chunk_scan's matrix cores consume), and final_state = b(nc-1) in float32.
+// The carried state stays in float32 registers for the whole pass.
+//
+// The recurrence is elementwise over the P x N state, so the state of one (batch, head)
+// is split across workgroups of one wave, each owning 256 elements (a float4 per lane),
+// giving batch * H * P * N / 256 independent waves.  The loads of b_intra for the next
+// kSP chunks do not depend on the carried state, so they are issued a whole group ahead
+// of the dependent multiply-adds; the pass is a pure HBM stream (read 4 bytes, write act
+// bytes per state element per chunk).
+//
+// b_intra and b_in use the tile order of the other kernels (see libssdscan.h); only
+// init_state / final_state use the row-major [P][N] order, so the thread owning tile
+// element (tile, lane l, r = 0..3) maps to p = 16 * pt + l % 16, n = 16 * nt + 4 (l / 16) + r.
+#include "ssd_common.h"
+
+namespace ssd {
+
+constexpr int kSP = 8;   // chunks whose loads are in flight together
+
+template <typename T>
+__device__ __forceinline__ void store_state(T *dst, const float4 &v);
+template <>
+__device__ __forceinline__ void store_state<float>(float *dst, const float4 &v) {
+    *reinterpret_cast<float4 *>(dst) = v;
+}
+template <>
+__device__ __forceinline__ void store_state<bf16>(bf16 *dst, const float4 &v) {
+    bf16x4 o;
+    o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
+    *reinterpret_cast<bf16x4 *>(dst) = o;
+}
+
+__device__ __forceinline__ float4 fma4(float a, const float4 &s, const float4 &b) {
+    return make_float4(fmaf(a, s.x, b.x), fmaf(a, s.y, b.y), fmaf(a, s.z, b.z), fmaf(a, s.w, b.w));
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void state_pass_kernel(Problem p) {
+    const int PN = p.P * p.N;
+    const int e4 = blockIdx.x * 64 + threadIdx.x;        // float4 index within one state
+    const int h = blockIdx.y, b = blockIdx.z;
+    if (e4 * 4 >= PN) return;
+    const int e = e4 * 4;
+    const int tile = e >> 8, l = (e >> 2) & 63;
+    const int PT = p.P >> 4;
+    const int pt = tile % PT, nt = tile / PT;
+    const int pp = pt * 16 + (l & 15), n0 = nt * 16 + 4 * (l >> 4);
+    const int64_t std_off = (((int64_t)b * p.H + h) * p.P + pp) * p.N + n0;
+
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.init) s = *reinterpret_cast<const float4 *>(p.init + std_off);
+
+    const int64_t cstride = (int64_t)p.H * PN;            // between chunks
+    const float *bi = p.b_intra + ((int64_t)b * p.nc * p.H + h) * PN + e;
+    T *bo = reinterpret_cast<T *>(p.b_in) + ((int64_t)b * p.nc * p.H + h) * PN + e;
+    typedef typename CumT<T>::type S;
+    const S *cum = reinterpret_cast<const S *>(p.dA_cum) + ((int64_t)b * p.H + h) * p.nc * p.Q + (p.Q - 1);
+
+    int c = 0;
+    for (; c + kSP <= p.nc; c += kSP) {
+        float4 v[kSP];
+        S d[kSP];
+#pragma unroll
+        for (int u = 0; u < kSP; ++u) {
+            v[u] = *reinterpret_cast<const float4 *>(bi + (c + u) * cstride);
+            d[u] = cum[(int64_t)(c + u) * p.Q];
+        }
+#pragma unroll
+        for (int u = 0; u < kSP; ++u) {
+            store_state<T>(bo + (c + u) * cstride, s);
+            s = fma4(expf((float)d[u]), s, v[u]);
+        }
+    }
+    for (; c < p.nc; ++c) {
+        const float4 v = *reinterpret_cast<const float4 *>(bi + c * cstride);
+        const S d = cum[(int64_t)c * p.Q];
+        store_state<T>(bo + c * cstride, s);
+        s = fma4(expf((float)d), s, v);
+    }
+    if (p.final_state) *reinterpret_cast<float4 *>(p.final_state + std_off) = s;
+}
+
+hipError_t launch_state_pass(const Problem &p, hipStream_t s) {
+    const int PN = p.P * p.N;
+    dim3 grid((PN / 4 + 63) / 64, p.H, p.batch);
+    if (p.dtype == 1) state_pass_kernel<bf16><<<grid, 64, 0, s>>>(p);
+    else state_pass_kernel<float><<<grid, 64, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,125 @@
+"""The C-ABI library: it loads, exports what the header declares, and rejects bad
+arguments on the host with the documented status codes (no GPU needed: every call here
+fails validation before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_linear_recurrence_amd import ssd, WORKLOADS
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "libssdscan.h")
+
+
+def _lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        pytest.skip("libssdscan.so not built")
+    return ssd.lib()
+
+
+def test_header_declares_exactly_the_exports():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text))
+    assert declared == set(ssd.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    L = _lib()
+    for name in ssd.EXPORTS:
+        assert hasattr(L, name), name
+    assert L.ssd_version() == 100
+    for code, name in ssd.STATUS.items():
+        assert L.ssd_status_string(code).decode() == name
+
+
+def _dims(b=1, L=256, H=2, P=16, N=16, G=1, dtype=0, reserved=0):
+    return ssd.Dims(b, L, H, P, N, G, dtype, reserved)
+
+
+FAKE = 1 << 40   # a 16-byte aligned address that is never dereferenced
+
+
+def _fwd(dims, x=FAKE, dt=FAKE + 2 ** 30, A=FAKE + 2 ** 31, B=FAKE + 2 ** 32, C=FAKE + 2 ** 33, D=None,
+         init=None, Q=64, y=FAKE + 2 ** 34, fin=None, flags=0, ws=FAKE + 2 ** 35, wsb=1 << 30):
+    L = _lib()
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    dp = None if dims is None else ctypes.byref(dims)
+    return L.ssd_chunk_scan_fwd(dp, v(x), v(dt), v(A), v(B), v(C), v(D), v(init), Q, v(y), v(fin),
+                                flags, v(ws), wsb, None)
+
+
+def test_fwd_argument_errors():
+    L = _lib()
+    assert _fwd(None) == 1
+    assert _fwd(_dims(dtype=7)) == 3
+    assert _fwd(_dims(reserved=1)) == 2
+    assert _fwd(_dims(H=3, G=2)) == 2
+    assert _fwd(_dims(L=0)) == 2
+    assert _fwd(_dims(), Q=0) == 2
+    assert _fwd(_dims(), Q=100) == 4                     # no kernel for Q = 100
+    assert _fwd(_dims(P=24)) == 4
+    assert _fwd(_dims(dtype=1, N=16)) == 4               # bf16 needs dstate >= 32
+    assert _fwd(_dims(), x=None) == 1
+    assert _fwd(_dims(), y=None) == 1
+    assert _fwd(_dims(), x=FAKE + 8) == 5
+    assert _fwd(_dims(), ws=None) == 6
+    assert _fwd(_dims(), wsb=16) == 6
+    assert _fwd(_dims(), y=FAKE + 64) == 8               # y overlaps x
+    assert _fwd(_dims(), flags=2) == 2
+    assert L.ssd_last_error_message().decode() != ""
+    # final_state may equal init_state, but not overlap it partially
+    assert _fwd(_dims(), init=FAKE + 2 ** 36, fin=FAKE + 2 ** 36 + 16) == 8
+
+
+def test_segmented_argument_errors():
+    L = _lib()
+    d = _dims(L=512)
+    v = ctypes.c_void_p
+
+    def seg(n_layers=2, V=128, states=FAKE + 2 ** 36, ws=FAKE + 2 ** 35, wsb=1 << 30, Q=64):
+        return L.ssd_chunk_scan_segmented(ctypes.byref(d), n_layers, V, v(FAKE), v(FAKE + 2 ** 30),
+                                          v(FAKE + 2 ** 31), v(FAKE + 2 ** 32), v(FAKE + 2 ** 33), None,
+                                          None if states is None else v(states), Q, 1,
+                                          v(FAKE + 2 ** 34), None if ws is None else v(ws), wsb, None)
+    assert seg(n_layers=0) == 2
+    assert seg(V=0) == 2
+    assert seg(states=None) == 1
+    assert seg(wsb=10) == 6
+    assert seg(Q=96) == 4
+
+
+def test_workspace_sizes_and_layout():
+    _lib()
+    for name, w in WORKLOADS.items():
+        d = ssd.Dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                     0 if w.dtype == "f32" else 1, 0)
+        assert ssd.shape_supported(d.dtype, w.chunk, w.headdim, w.dstate), name
+        nb = ssd.workspace_bytes(d, w.chunk)
+        offs = ssd.workspace_layout(d, w.chunk)
+        e = 4 if w.dtype == "f32" else 2
+        states = w.batch * w.nchunks * w.nheads * w.headdim * w.dstate
+        assert offs[0] == 0 and offs[1] >= w.batch * w.nheads * w.nchunks * w.chunk * 4
+        assert offs[2] - offs[1] >= states * 4 and offs[3] - offs[2] >= states * e
+        assert all(o % 256 == 0 for o in offs) and nb == offs[3]
+        if w.segment:
+            segb = ssd.segmented_workspace_bytes(d, w.chunk, w.segment)
+            # memory depends on V, not on the sequence length
+            d2 = ssd.Dims(w.batch, 4 * w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d.dtype, 0)
+            assert ssd.segmented_workspace_bytes(d2, w.chunk, w.segment) == segb
+            assert segb < nb
+    assert ssd.workspace_bytes(_dims(H=3, G=2), 64) == 0
+
+
+def test_tile_order_reindex_is_a_permutation():
+    P, N = 32, 64
+    t = torch.arange(P * N, dtype=torch.float64)
+    m = ssd.tile_order_to_pn(t, P, N)
+    assert sorted(m.reshape(-1).tolist()) == t.tolist()
+    # tile (nt=1, pt=0), lane 17 (g=1, col=1), r=2 -> p=1, n=16+4+2
+    idx = ((1 * (P // 16) + 0) * 64 + 17) * 4 + 2
+    assert m[1, 22].item() == idx

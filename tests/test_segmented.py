@@ -1,0 +1,109 @@
+"""GPU tests of the vertical (segmented) layer stack [分块推理 §3.2] of the page
+"分块推理：解锁循环模型并行计算，实现长序列高效处理": bit-identical to the horizontal order
+[分块推理 §3.1] when V is a multiple of Q, resumable from host copies of the per-layer
+states, and within tolerance of the fp64 stack oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_linear_recurrence_amd import inputs, ssd, WORKLOADS
+
+from helpers import err_bf16, err_f32, to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _stack(nl, b, L, H, P, N, dtype="bf16", seed=0):
+    return inputs.make_stack(b, L, H, P, N, 1, nl, dtype, seed=seed)
+
+
+def test_small_stack_matches_oracle_and_horizontal():
+    nl, b, L, H, P, N, Q, V = 4, 2, 1000, 3, 64, 64, 64, 256
+    d = _stack(nl, b, L, H, P, N)
+    g = to_dev(d, DEV)
+    s_seg = torch.zeros(nl, b, H, P, N, device=DEV)
+    y_seg, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_seg, V, Q)
+    s_hor = torch.zeros_like(s_seg)
+    y_hor, _ = ssd.horizontal(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_hor, Q)
+    torch.cuda.synchronize()
+    assert torch.equal(y_seg, y_hor)
+    assert torch.equal(s_seg, s_hor)
+    yr, fr = oracle.stack_horizontal(d["x0"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    assert err_bf16(y_seg, yr) <= 2e-2
+    for l in range(nl):
+        assert err_bf16(s_seg[l], fr[l]) <= 2e-2
+
+
+def test_fp32_stack_and_ragged_segments():
+    nl, b, L, H, P, N, Q = 3, 1, 700, 2, 16, 16, 64
+    d = _stack(nl, b, L, H, P, N, dtype="f32", seed=1)
+    g = to_dev(d, DEV)
+    yr, fr = oracle.stack_horizontal(d["x0"], d["dt"], d["A"], d["B"], d["C"], d["D"], store_bf16=False)
+    for V in (64, 128, 100, 700, 5000):            # 100 is not a multiple of Q
+        s = torch.zeros(nl, b, H, P, N, device=DEV)
+        y, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s, V, Q)
+        torch.cuda.synchronize()
+        assert err_f32(y, yr) <= 1e-4, V
+        for l in range(nl):
+            assert err_f32(s[l], fr[l]) <= 1e-4, (V, l)
+
+
+def test_resume_from_host_copy_is_bit_identical():
+    """Stop after some segments, round-trip the per-layer states through host memory,
+    continue: the result equals one uninterrupted call bit for bit."""
+    nl, b, L, H, P, N, Q, V = 3, 1, 2048, 4, 64, 128, 256, 512
+    d = _stack(nl, b, L, H, P, N, seed=2)
+    g = to_dev(d, DEV)
+    s_full = torch.zeros(nl, b, H, P, N, device=DEV)
+    y_full, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_full, V, Q)
+    cut = 1024
+    s = torch.zeros(nl, b, H, P, N, device=DEV)
+    y1, _ = ssd.segmented(g["x0"][:, :cut].contiguous(), g["dt"][:, :cut].contiguous(), g["A"],
+                          g["B"][:, :cut].contiguous(), g["C"][:, :cut].contiguous(), g["D"], s, V, Q)
+    host = s.cpu()
+    del s
+    s2 = host.to(DEV)
+    y2, _ = ssd.segmented(g["x0"][:, cut:].contiguous(), g["dt"][:, cut:].contiguous(), g["A"],
+                          g["B"][:, cut:].contiguous(), g["C"][:, cut:].contiguous(), g["D"], s2, V, Q)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], dim=1), y_full)
+    assert torch.equal(s2, s_full)
+
+
+def test_swapped_layer_states_change_the_output():
+    nl, b, L, H, P, N, Q, V = 2, 1, 512, 2, 64, 64, 64, 128
+    d = _stack(nl, b, L, H, P, N, seed=3)
+    g = to_dev(d, DEV)
+    init = torch.randn(nl, b, H, P, N, device=DEV)
+    y, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], init.clone(), V, Q)
+    y_sw, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], init.flip(0).clone(), V, Q)
+    torch.cuda.synchronize()
+    assert not torch.equal(y, y_sw)
+
+
+def test_vertical_stack_workload():
+    """24 layers, 32768 tokens, V = 2048: segmented == horizontal bit for bit; the oracle
+    checks every head on the first two segments and one head over the whole sequence."""
+    w = WORKLOADS["vertical_stack_24x_L32768_V2048"]
+    d = inputs.make(w)
+    g = to_dev(d, DEV)
+    nl = w.layers
+    shp = (nl, w.batch, w.nheads, w.headdim, w.dstate)
+    s_seg = torch.zeros(shp, device=DEV)
+    y_seg, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_seg, w.segment, w.chunk)
+    s_hor = torch.zeros(shp, device=DEV)
+    y_hor, _ = ssd.horizontal(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_hor, w.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(y_seg, y_hor)
+    assert torch.equal(s_seg, s_hor)
+    T = 2 * w.segment
+    yr, _ = oracle.stack_horizontal(d["x0"][:, :T], d["dt"][:, :T], d["A"], d["B"][:, :T], d["C"][:, :T],
+                                    d["D"])
+    assert err_bf16(y_seg[:, :T], yr) <= 2e-2
+    h = int(np.argmax(d["A"][0].numpy()))
+    yr1, fr1 = oracle.stack_horizontal(d["x0"][:, :, [h]], d["dt"][:, :, [h]], d["A"][:, [h]], d["B"],
+                                       d["C"], d["D"][:, [h]])
+    assert err_bf16(y_seg[:, :, [h]], yr1) <= 2e-2
+    assert err_bf16(s_seg[:, :, [h]], fr1) <= 2e-2
