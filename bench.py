@@ -1,7 +1,7 @@
 """Throughput of the chunked SSD scan on one MI355X, as one JSON line.
 
-A step is one ssd_chunk_scan_fwd call (all four kernels: chunk_cumsum, chunk_state,
-state_pass, chunk_scan) over the whole batch of the 128K-token workload
+A step is one ssd_chunk_scan_fwd call (all five kernels: chunk_cumsum, chunk_state,
+state_pass, chunk_cb, chunk_scan) over the whole batch of the 128K-token workload
 (long_context_b1_L131072_h48: batch 1, L 131072, H 48, P 64, N 128, Q 256, bf16), with
 every input already resident in HBM.  W untimed warm-up steps, then exactly K timed
 steps between two device synchronisations.
@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=0, help="launches per kernel for per-kernel timing "
                     "(default: --steps)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -56,11 +58,14 @@ def alg_bytes(w):
     cum = b * H * nc * Q * cum_e
     states = b * nc * H * P * N
     init = final = b * H * P * N * 4
+    nrb = Q // 16
+    cbt = b * nc * G * nrb * (nrb + 1) // 2 * 256 * e   # causal C.B^T tiles
     k = {
         "chunk_cumsum": dt + cum,
         "chunk_state": x + bc + cum + states * 4,
         "state_pass": states * 4 + states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
-        "chunk_scan": x + 2 * bc + cum + states * e + y,
+        "chunk_cb": 2 * bc + cbt,
+        "chunk_scan": x + bc + cum + states * e + cbt + y,
     }
     method = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final + 2 * states * 4 + 2 * states * e
     return k, method
@@ -70,8 +75,10 @@ def alg_flops(w):
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nc = w.nchunks
     per_chunk_state = H * 2 * Q * N * P
-    per_chunk_scan = H * (Q * (Q + 1) * P + 2 * Q * N * P) + G * Q * (Q + 1) * N
-    return {"chunk_state": b * nc * per_chunk_state, "chunk_scan": b * nc * per_chunk_scan}
+    per_chunk_scan = H * (Q * (Q + 1) * P + 2 * Q * N * P)
+    per_chunk_cb = G * Q * (Q + 1) * N
+    return {"chunk_state": b * nc * per_chunk_state, "chunk_cb": b * nc * per_chunk_cb,
+            "chunk_scan": b * nc * per_chunk_scan}
 
 
 def cpu_baseline(d, w):
@@ -116,7 +123,7 @@ def main():
     fin = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(first=1, last=4):
+    def step(first=1, last=ssd.NSTAGES):
         ssd.fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["init_state"], w.chunk, y=y,
                 final_state=fin, workspace=ws, stream=stream, first_stage=first, last_stage=last)
 
@@ -138,7 +145,7 @@ def main():
     tokens_per_s = w.tokens / (ms_step * 1e-3)
 
     # per-kernel durations: HIP events around each single-kernel launch on the same stream
-    names = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_scan"]
+    names = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_cb", "chunk_scan"]
     kb, method_bytes = alg_bytes(w)
     kf = alg_flops(w)
     ksteps = args.kernel_steps or args.steps
@@ -181,6 +188,13 @@ def main():
         "kernels": kernels,
         "wall_s_timed": round(wall, 4),
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, w)

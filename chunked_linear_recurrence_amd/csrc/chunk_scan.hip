@@ -1,4 +1,4 @@
-// chunk_scan: every chunk's output, [分块推理 §2.1-§2.2] of the page
+// chunk_cb and chunk_scan: every chunk's output, [分块推理 §2.1-§2.2] of the page
 // "分块推理：解锁循环模型并行计算，实现长序列高效处理":
 //
 //   by_intra_i = sum_{j <= i} (C_i . B_j) exp(cum_i - cum_j) x_j      (zero-state intra part)
@@ -8,24 +8,32 @@
 // rounded once to the activation dtype.  cum is the chunk's dA_cum row and b(c-1) is
 // b_in[c] from state_pass.
 //
-// Work: one workgroup of Q/32 waves per (batch, chunk, group of heads that read the same
-// B/C).  The chunk is cut into Q/16 row blocks of 16 tokens; wave w owns row blocks
-// w and Q/16-1-w, so every wave has the same number (Q/16 + 1) of causal 16x16 tiles.
-//  1. Once per workgroup: S^T = B_c C_c^T restricted to the causal tiles, on the matrix
-//     cores, kept in registers.  It is shared by every head of the group (the decay mask
-//     is applied per head afterwards), so C.B^T is computed once per group, not per head.
-//     C fragments for the wave's rows also stay in registers.
-//  2. Per head: x is transposed into LDS (tokens contiguous per channel), b_in (tile
-//     order, read linearly) and the cum row are copied to LDS; double-buffered, with the
-//     next head's loads in flight during the current head's products.
-//     Z = C b(c-1)^T on the matrix cores, scaled by exp(cum_i) per row, then
-//     acc += (S^T . decay)^T x, where each S^T tile is multiplied by exp(cum_i - cum_j)
-//     (masked to j <= i) in fp32, rounded to the operand dtype and used directly as the
-//     A operand (a lane's 4 consecutive output rows are 4 consecutive k values).
-//  3. Epilogue adds D x (and x), rounds, stores y.
-// Tiles are paired into 16x16x32 bf16 products (16x16x4 f32 for the fp32 dtype); the
-// slot list of a wave is padded with one zero tile so pairs never straddle its two row
-// blocks.
+// Both kernels cut a chunk into Q/16 row blocks of 16 tokens and use Q/32 waves; wave w
+// owns row blocks I0 = w and I1 = Q/16-1-w, so every wave has the same number (Q/16 + 1)
+// of causal 16x16 tiles (J <= I).  The wave's tile list ("slots") is: slot s <= w is
+// (I0, J = s), slot w + 1 is a zero pad, slot s >= w + 2 is (I1, J = s - w - 2); the pad
+// keeps pairs of slots inside one row block.  The wave index is read as a scalar, so
+// every choice that depends on it is a uniform branch.
+//
+// chunk_cb (once per chunk and B/C group, shared by all heads of the group):
+//   S^T = B_c C_c^T on the matrix cores for the causal tiles, zero above the diagonal,
+//   stored in the operand dtype in tile order: tile (I, J) at index I(I+1)/2 + J, lane
+//   (col, g) value r holding S^T[16J + 4g + r][16I + col].
+// chunk_scan (one workgroup per chunk and head):
+//   x is transposed into LDS (tokens contiguous per channel), b_in copied, and three
+//   per-token factors computed once:  cum_j,  F_j = exp(cum_end(j) - cum_j),
+//   G_j = exp(cum_j), where end(j) is the last token of j's 16-token block.  The products
+//   are computed transposed (y^T[p][i]) so that a lane's 4 accumulator values are 4
+//   consecutive channels of one token and leave as one 8-byte store:
+//     Z^T = b(c-1) C^T, column i scaled by G_i;
+//     y^T += x^T (S^T . decay), where an off-diagonal tile (J < I) factorises the decay as
+//       exp(cum_i - cum_j) = exp(cum_i - cum_end(J)) * F_j (both factors <= 1, one exp per
+//       lane and tile) and the diagonal tile uses exp(min(cum_i - cum_j, 0)) (the zeroed
+//       upper triangle of S^T does the masking); a lane's 4 S^T values are 4 consecutive
+//       k values of the B operand, so no data moves between lanes;
+//     y^T += x^T diag(D + residual) on the matrix cores (D split in a high and a low bf16
+//       part so the skip term keeps fp32 accuracy).
+// Tiles are paired into 16x16x32 bf16 products (16x16x4 f32 for the fp32 dtype).
 #include "ssd_common.h"
 
 namespace ssd {
@@ -34,43 +42,315 @@ template <typename T, int Q, int P, int N>
 struct ScanCfg {
     static constexpr int NRB = Q / 16, NW = NRB / 2, THREADS = NW * 64;
     static constexpr int NSLOT = NRB + 2, NPAIR = NSLOT / 2;
+    static constexpr int NTRI = NRB * (NRB + 1) / 2;            // causal tiles per chunk
     static constexpr int PT = P / 16, NT = N / 16;
-    static constexpr int RS = Q + 4;
-    static constexpr int RJ = 16 / (int)sizeof(T);
-    static constexpr int XB = (Q / RJ) * (P / 4);
-    static constexpr int XBT = (XB + THREADS - 1) / THREADS;
-    static constexpr int SV = P * N * (int)sizeof(T) / 16;       // 16-byte vectors of b_in
-    static constexpr int SVT = (SV + THREADS - 1) / THREADS;
-    static constexpr int CT = (Q + THREADS - 1) / THREADS;
-    static constexpr int XT_BYTES = P * RS * (int)sizeof(T);
-    static constexpr int ST_BYTES = P * N * (int)sizeof(T);
-    static constexpr int BUF_BYTES = XT_BYTES + ST_BYTES + Q * (int)sizeof(typename CumT<T>::type);
-    static constexpr bool DB = 2 * BUF_BYTES <= kLdsBytes;
-    static constexpr int LDS = DB ? 2 * BUF_BYTES : BUF_BYTES;
-    static constexpr bool OK = BUF_BYTES <= kLdsBytes && (sizeof(T) == 4 || NT % 2 == 0) &&
-                               (Q == 64 || Q == 128 || Q == 256);
+    static constexpr int BROW = N + (sizeof(T) == 2 ? 8 : 4);    // staged B row stride (chunk_cb)
+    static constexpr int BV = Q * N * (int)sizeof(T) / 16;       // 16-byte vectors of B
+    static constexpr int HEAD_BYTES = Q * P * (int)sizeof(T) + P * N * (int)sizeof(T) +
+                                      Q * (int)sizeof(typename CumT<T>::type) + 2 * Q * 4;
+    static constexpr bool DB = 2 * HEAD_BYTES <= kLdsBytes;     // double-buffered head data
+    static constexpr int LDS = DB ? 2 * HEAD_BYTES : HEAD_BYTES;
+    static constexpr int CB_LDS = Q * BROW * (int)sizeof(T);
+    static constexpr bool OK = LDS <= kLdsBytes && CB_LDS <= kLdsBytes &&
+                               (sizeof(T) == 4 || NT % 2 == 0) && (Q == 64 || Q == 128 || Q == 256) &&
+                               P * (int)sizeof(T) >= 32;
 };
 
-template <typename T, int RJ>
-__device__ __forceinline__ void scan_load_block(const T *base, int64_t pitch, int j0, int c0, int rows,
-                                                typename TF<T>::type (&r)[RJ]) {
+// Slot s of wave w: row block, column block, pad flag (all uniform).
+struct Slot {
+    int I, J;
+    bool pad, first;
+};
+__device__ __forceinline__ Slot slot_of(int s, int w, int NRB) {
+    Slot r;
+    r.pad = s == w + 1;
+    r.first = s <= w;
+    r.I = r.first ? w : NRB - 1 - w;
+    r.J = r.pad ? 0 : (r.first ? s : s - w - 2);
+    return r;
+}
+
+// ---------------------------------------------------------------------------------
+// chunk_cb: causal S^T tiles of one (batch, chunk, group)
+// ---------------------------------------------------------------------------------
+template <typename T, int Q, int N>
+__global__ __launch_bounds__((Q / 32) * 64) void chunk_cb_kernel(Problem p) {
+    using Cfg = ScanCfg<T, Q, 16, N>;
+    using F = typename TF<T>::type;
+    constexpr int THREADS = Cfg::THREADS, BROW = Cfg::BROW, NRB = Cfg::NRB, NT = Cfg::NT;
+    constexpr int NSTEP = sizeof(T) == 2 ? 2 : 1;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g4 = 4 * (lane >> 4);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);     // (b, c, grp)
+    const int grp = logical % p.G;
+    const int bc = logical / p.G;
+    const int c = bc % p.nc, b = bc / p.nc;
+    const int t0 = c * Q;
+    const int Qc = min(Q, p.L - t0);
+    const int64_t bcp = (int64_t)p.G * N;
+    const T *Cb = reinterpret_cast<const T *>(p.C) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
+    const T *Bb = reinterpret_cast<const T *>(p.B) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
+    const int I0 = w, I1 = NRB - 1 - w;
+
+    T *bs = reinterpret_cast<T *>(smem);
+    {
+        constexpr int VPR = N * (int)sizeof(T) / 16;
+        for (int v = tid; v < Cfg::BV; v += THREADS) {
+            const int j = v / VPR, q = v % VPR;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (j < Qc) val = *reinterpret_cast<const uint4 *>(Bb + (int64_t)j * bcp + q * (16 / (int)sizeof(T)));
+            *reinterpret_cast<uint4 *>(bs + j * BROW + q * (16 / (int)sizeof(T))) = val;
+        }
+    }
+    F cf[2][NT];
 #pragma unroll
-    for (int i = 0; i < RJ; ++i) {
-        if (j0 + i < rows) r[i] = *reinterpret_cast<const typename TF<T>::type *>(base + (int64_t)(j0 + i) * pitch + c0);
-        else r[i] = zero_frag<typename TF<T>::type>();
+    for (int ri = 0; ri < 2; ++ri) {
+        const int i = (ri ? I1 : I0) * 16 + col;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            cf[ri][nt] = (i < Qc) ? *reinterpret_cast<const F *>(Cb + (int64_t)i * bcp + nt * 16 + g4)
+                                  : zero_frag<F>();
+    }
+    __syncthreads();
+
+    float *out = reinterpret_cast<float *>(p.cb) + (int64_t)logical * Cfg::NTRI * 256;
+#pragma unroll
+    for (int s = 0; s < Cfg::NSLOT; ++s) {
+        const Slot sl = slot_of(s, w, NRB);
+        if (sl.pad) continue;
+        f32x4 t = zero_frag<f32x4>();
+        const T *brow = bs + (sl.J * 16 + col) * BROW + g4;
+        if (sl.first) {
+#pragma unroll
+            for (int nt = 0; nt < NT; nt += NSTEP) {
+                if constexpr (sizeof(T) == 2)
+                    t = mma_pair(*reinterpret_cast<const F *>(brow + nt * 16), cf[0][nt],
+                                 *reinterpret_cast<const F *>(brow + (nt + 1) * 16), cf[0][nt + 1], t);
+                else
+                    t = mma_one(*reinterpret_cast<const F *>(brow + nt * 16), cf[0][nt], t);
+            }
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < NT; nt += NSTEP) {
+                if constexpr (sizeof(T) == 2)
+                    t = mma_pair(*reinterpret_cast<const F *>(brow + nt * 16), cf[1][nt],
+                                 *reinterpret_cast<const F *>(brow + (nt + 1) * 16), cf[1][nt + 1], t);
+                else
+                    t = mma_one(*reinterpret_cast<const F *>(brow + nt * 16), cf[1][nt], t);
+            }
+        }
+        if (sl.J == sl.I) {                                     // uniform: diagonal tile
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t[r] = (g4 + r <= col) ? t[r] : 0.f;
+        }
+        const int tri = sl.I * (sl.I + 1) / 2 + sl.J;
+        *reinterpret_cast<f32x4 *>(out + (tri * 64 + lane) * 4) = t;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// chunk_scan: one (batch, chunk, group of heads)
+// ---------------------------------------------------------------------------------
+// Raw LDS pointers for the gfx950 LDS-DMA and transpose-read builtins.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// 16-byte global -> LDS copy: lane l of the wave writes lds_base + 16 * l.
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 0);
+}
+
+// x tile in LDS: row-major [Q][P] in 16-byte pieces; piece q of row r is stored at
+// position q ^ swz(r) of that row, which spreads the 4 rows read by one transpose load
+// over different banks.
+template <int PIECES>
+__device__ __forceinline__ int x_swz(int r) { return (((r >> 1) & 3) << 1) & (PIECES - 1); }
+
+// A operand fragment of x^T for (16-token block J, 16-channel tile pt): lane (col, g) gets
+// x[16J + 4g + e][16pt + col], e = 0..3.
+template <typename T, int P>
+__device__ __forceinline__ typename TF<T>::type x_frag(const unsigned char *xs, int J, int pt, int lane);
+
+template <>
+__device__ __forceinline__ bf16x4 x_frag<bf16, 16>(const unsigned char *xs, int J, int pt, int lane) {
+    constexpr int P = 16, PIECES = P * 2 / 16;
+    const int s = lane & 15, g = lane >> 4;
+    const int r = J * 16 + 4 * g + (s >> 2);
+    const int c = pt * 16 + 4 * (s & 3);
+    const int q = (c >> 3) ^ x_swz<PIECES>(r);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(xs + r * (P * 2) + q * 16 + (c & 7) * 2));
+}
+#define SSD_XFRAG_BF16(PP)                                                                           \
+    template <>                                                                                      \
+    __device__ __forceinline__ bf16x4 x_frag<bf16, PP>(const unsigned char *xs, int J, int pt, int lane) { \
+        constexpr int PIECES = PP * 2 / 16;                                                          \
+        const int s = lane & 15, g = lane >> 4;                                                      \
+        const int r = J * 16 + 4 * g + (s >> 2);                                                     \
+        const int c = pt * 16 + 4 * (s & 3);                                                         \
+        const int q = (c >> 3) ^ x_swz<PIECES>(r);                                                   \
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(xs + r * (PP * 2) + q * 16 + (c & 7) * 2)); \
+    }
+SSD_XFRAG_BF16(32)
+SSD_XFRAG_BF16(64)
+SSD_XFRAG_BF16(128)
+#undef SSD_XFRAG_BF16
+
+// fp32: no transpose load for 32-bit data; four scalar reads (no swizzle for fp32 tiles).
+#define SSD_XFRAG_F32(PP)                                                                            \
+    template <>                                                                                      \
+    __device__ __forceinline__ f32x4 x_frag<float, PP>(const unsigned char *xs, int J, int pt, int lane) { \
+        const int col = lane & 15, g = lane >> 4;                                                    \
+        const float *base = reinterpret_cast<const float *>(xs) + (J * 16 + 4 * g) * PP + pt * 16 + col; \
+        f32x4 v;                                                                                     \
+        v[0] = base[0]; v[1] = base[PP]; v[2] = base[2 * PP]; v[3] = base[3 * PP];                   \
+        return v;                                                                                    \
+    }
+SSD_XFRAG_F32(16)
+SSD_XFRAG_F32(32)
+SSD_XFRAG_F32(64)
+SSD_XFRAG_F32(128)
+#undef SSD_XFRAG_F32
+
+template <typename T, int Q, int P, int N>
+struct HeadBuf {
+    typedef typename CumT<T>::type S;
+    static constexpr int X = Q * P * (int)sizeof(T);
+    static constexpr int ST = P * N * (int)sizeof(T);
+    static constexpr int CM = Q * (int)sizeof(S);
+    static constexpr int FG = Q * 4;
+    static constexpr int O_ST = X, O_CM = X + ST, O_F = X + ST + CM, O_G = O_F + FG;
+    static constexpr int BYTES = O_G + FG;
+};
+
+// Per-head products of wave W (all slot choices and offsets are compile-time):
+// Z^T scaled by G, the decayed S^T tiles times x^T, and (D + res) x.
+template <typename T, int Q, int P, int N, int W>
+__device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 (&sT)[ScanCfg<T, Q, P, N>::NSLOT],
+                                      const typename TF<T>::type (&cf)[2][ScanCfg<T, Q, P, N>::NT],
+                                      float dres, int lane, f32x4 (&acc)[2][ScanCfg<T, Q, P, N>::PT]) {
+    using Cfg = ScanCfg<T, Q, P, N>;
+    using Buf = HeadBuf<T, Q, P, N>;
+    using F = typename TF<T>::type;
+    typedef typename CumT<T>::type S;
+    constexpr int NRB = Cfg::NRB, PT = Cfg::PT, NT = Cfg::NT;
+    constexpr int NSTEP = sizeof(T) == 2 ? 2 : 1;
+    constexpr int w = W, I0 = W, I1 = NRB - 1 - W;
+    const int col = lane & 15, g4 = 4 * (lane >> 4);
+    const unsigned char *xs = buf;
+    const T *stb = reinterpret_cast<const T *>(buf + Buf::O_ST);
+    const S *cm = reinterpret_cast<const S *>(buf + Buf::O_CM);
+    const float *Fv = reinterpret_cast<const float *>(buf + Buf::O_F);
+    const float *Gv = reinterpret_cast<const float *>(buf + Buf::O_G);
+
+    // Output tiles are transposed: acc[ri][pt] lane (col, g), value r holds
+    // y^T[p = pt*16 + 4g + r][i = I*16 + col].
+    // Z^T = b(c-1) C^T, then column i scaled by G_i = exp(cum_i)
+#pragma unroll
+    for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[ri][pt] = zero_frag<f32x4>();
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; nt += NSTEP) {
+            const F s0 = *reinterpret_cast<const F *>(stb + ((nt * PT + pt) * 64 + lane) * 4);
+            if constexpr (sizeof(T) == 2) {
+                const F s1 = *reinterpret_cast<const F *>(stb + (((nt + 1) * PT + pt) * 64 + lane) * 4);
+#pragma unroll
+                for (int ri = 0; ri < 2; ++ri)
+                    acc[ri][pt] = mma_pair(s0, cf[ri][nt], s1, cf[ri][nt + 1], acc[ri][pt]);
+            } else {
+#pragma unroll
+                for (int ri = 0; ri < 2; ++ri) acc[ri][pt] = mma_one(s0, cf[ri][nt], acc[ri][pt]);
+            }
+        }
+    }
+    const S ci0 = cm[I0 * 16 + col], ci1 = cm[I1 * 16 + col];
+    {
+        const float gi0 = Gv[I0 * 16 + col], gi1 = Gv[I1 * 16 + col];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc[0][pt][r] *= gi0;
+                acc[1][pt][r] *= gi1;
+            }
+    }
+
+    // by_intra: pairs of slots, each pair feeding one of the two row blocks
+#pragma unroll
+    for (int q = 0; q < Cfg::NPAIR; ++q) {
+        F a[2];
+        int Jx[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int s = 2 * q + u;
+            const Slot sl = slot_of(s, w, NRB);
+            const S ci = sl.first ? ci0 : ci1;
+            Jx[u] = sl.J;
+            f32x4 m;
+            if (sl.J < sl.I) {                              // uniform: off-diagonal tile or pad
+                const float e = __expf((float)(ci - cm[sl.J * 16 + 15]));
+                const f32x4 fj = *reinterpret_cast<const f32x4 *>(Fv + sl.J * 16 + g4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] = sT[s][r] * (e * fj[r]);
+            } else {                                        // diagonal (masked in S^T)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    m[r] = sT[s][r] * __expf(fminf((float)(ci - cm[sl.J * 16 + g4 + r]), 0.f));
+            }
+            a[u] = frag_from_f32<T>(m);
+        }
+        const bool owner1 = (2 * q) >= (w + 1);             // uniform
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const F x0 = x_frag<T, P>(xs, Jx[0], pt, lane);
+            const F x1 = x_frag<T, P>(xs, Jx[1], pt, lane);
+            if (owner1) acc[1][pt] = mma_pair(x0, a[0], x1, a[1], acc[1][pt]);
+            else acc[0][pt] = mma_pair(x0, a[0], x1, a[1], acc[0][pt]);
+        }
+    }
+
+    // + (D + residual) x on the matrix cores: B operand diag(D + res) split into a high
+    // and a low part in the operand dtype, A operand the x fragments of the diagonal block.
+    {
+        F dhi, dlo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = (g4 + e == col) ? dres : 0.f;
+            dhi[e] = from_f32<T>(v);
+            dlo[e] = from_f32<T>(v - to_f32(dhi[e]));
+        }
+#pragma unroll
+        for (int ri = 0; ri < 2; ++ri) {
+            const int I = ri ? I1 : I0;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const F xv = x_frag<T, P>(xs, I, pt, lane);
+                if constexpr (sizeof(T) == 2) acc[ri][pt] = mma_pair(xv, dhi, xv, dlo, acc[ri][pt]);
+                else acc[ri][pt] = mma_one(xv, dhi, acc[ri][pt]);
+            }
+        }
     }
 }
 
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_kernel(Problem p) {
     using Cfg = ScanCfg<T, Q, P, N>;
+    using Buf = HeadBuf<T, Q, P, N>;
     using F = typename TF<T>::type;
     typedef typename CumT<T>::type S;
-    constexpr int RJ = Cfg::RJ, RS = Cfg::RS, THREADS = Cfg::THREADS;
+    constexpr int THREADS = Cfg::THREADS, NW = Cfg::NW;
     constexpr int NRB = Cfg::NRB, NSLOT = Cfg::NSLOT, PT = Cfg::PT, NT = Cfg::NT;
+    constexpr int NSTEP = sizeof(T) == 2 ? 2 : 1;
+    constexpr int XPIECES = P * (int)sizeof(T) / 16;          // 16-byte pieces per x row
     extern __shared__ __align__(16) unsigned char smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int col = lane & 15, g4 = 4 * (lane >> 4);
     const int hpg = p.H / p.G;
     const int hg_per_group = (hpg + p.heads_per_wg_scan - 1) / p.heads_per_wg_scan;
@@ -86,224 +366,132 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     const int Qc = min(Q, p.L - t0);
     const int HP = p.H * P;
     const int64_t PN = (int64_t)P * N;
-    const int64_t bcp = (int64_t)p.G * N;                    // B/C row pitch
-    const T *Cb = reinterpret_cast<const T *>(p.C) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
-    const T *Bb = reinterpret_cast<const T *>(p.B) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
+    const int64_t bcp = (int64_t)p.G * N;
     const int I0 = w, I1 = NRB - 1 - w;
 
-    // ---- C fragments of the wave's two row blocks (A operand of Z, B operand of S^T)
+    // ---- per-lane byte offsets of this thread's DMA pieces (same for every head)
+    constexpr int XK = (Q * XPIECES + THREADS - 1) / THREADS;
+    int xoff[XK];
+#pragma unroll
+    for (int k = 0; k < XK; ++k) {
+        const int piece = (k * NW + w) * 64 + lane;            // LDS piece written by this lane
+        const int r = piece / XPIECES, qp = piece % XPIECES;
+        const int q = qp ^ (sizeof(T) == 2 ? x_swz<XPIECES>(r) : 0);
+        const int rr = min(r, Qc - 1);                          // rows past a short chunk repeat the last
+        xoff[k] = (rr * HP) * (int)sizeof(T) + q * 16;
+    }
+    const unsigned char *xchunk = reinterpret_cast<const unsigned char *>(p.x) +
+                                  ((int64_t)b * p.x_bs + (int64_t)t0 * HP) * (int64_t)sizeof(T);
+    auto issue = [&](int h, unsigned char *buf) {
+        const unsigned char *xh = xchunk + (int64_t)h * P * sizeof(T);
+#pragma unroll
+        for (int k = 0; k < XK; ++k)
+            if ((k * NW + w) * 64 + lane < Q * XPIECES)
+                dma16(xh + xoff[k], buf + (k * NW + w) * 1024);
+        const unsigned char *sv = reinterpret_cast<const unsigned char *>(p.b_in) +
+                                  (((int64_t)b * p.nc + c) * p.H + h) * PN * (int64_t)sizeof(T);
+        constexpr int SP = Buf::ST / 16;
+#pragma unroll
+        for (int k = 0; k < (SP + THREADS - 1) / THREADS; ++k)
+            if ((k * NW + w) * 64 + lane < SP)
+                dma16(sv + ((k * NW + w) * 64 + lane) * 16, buf + Buf::O_ST + (k * NW + w) * 1024);
+        const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
+        const unsigned char *cs = reinterpret_cast<const unsigned char *>(reinterpret_cast<const S *>(p.dA_cum) + tok);
+        constexpr int CP = Buf::CM / 16;
+#pragma unroll
+        for (int k = 0; k < (CP + THREADS - 1) / THREADS; ++k)
+            if ((k * NW + w) * 64 + lane < CP)
+                dma16(cs + ((k * NW + w) * 64 + lane) * 16, buf + Buf::O_CM + (k * NW + w) * 1024);
+        constexpr int FP = Buf::FG / 16;
+        const unsigned char *fs = reinterpret_cast<const unsigned char *>(p.decF + tok);
+        const unsigned char *gs = reinterpret_cast<const unsigned char *>(p.decG + tok);
+#pragma unroll
+        for (int k = 0; k < (FP + THREADS - 1) / THREADS; ++k)
+            if ((k * NW + w) * 64 + lane < FP) {
+                dma16(fs + ((k * NW + w) * 64 + lane) * 16, buf + Buf::O_F + (k * NW + w) * 1024);
+                dma16(gs + ((k * NW + w) * 64 + lane) * 16, buf + Buf::O_G + (k * NW + w) * 1024);
+            }
+    };
+    issue(h0, smem);
+
+    // ---- per workgroup: this wave's S^T tiles (float) and C fragments
+    f32x4 sT[NSLOT];
+    {
+        const float *cbt = reinterpret_cast<const float *>(p.cb) + ((int64_t)bc * p.G + grp) * Cfg::NTRI * 256;
+#pragma unroll
+        for (int s = 0; s < NSLOT; ++s) {
+            const Slot sl = slot_of(s, w, NRB);
+            const int tri = sl.I * (sl.I + 1) / 2 + sl.J;
+            sT[s] = sl.pad ? zero_frag<f32x4>() : *reinterpret_cast<const f32x4 *>(cbt + (tri * 64 + lane) * 4);
+        }
+    }
     F cf[2][NT];
+    {
+        const T *Cb = reinterpret_cast<const T *>(p.C) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
 #pragma unroll
-    for (int ri = 0; ri < 2; ++ri) {
-        const int i = (ri ? I1 : I0) * 16 + col;
+        for (int ri = 0; ri < 2; ++ri) {
+            const int i = (ri ? I1 : I0) * 16 + col;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            cf[ri][nt] = (i < Qc) ? *reinterpret_cast<const F *>(Cb + (int64_t)i * bcp + nt * 16 + g4)
-                                  : zero_frag<F>();
+            for (int nt = 0; nt < NT; ++nt)
+                cf[ri][nt] = (i < Qc) ? *reinterpret_cast<const F *>(Cb + (int64_t)i * bcp + nt * 16 + g4)
+                                      : zero_frag<F>();
+        }
     }
 
-    // ---- prefetch of one head's x rows, b_in vectors and cum row
-    F xr[Cfg::XBT][RJ];
-    uint4 sr[Cfg::SVT];
-    S cr[Cfg::CT];
-    const T *xbase = reinterpret_cast<const T *>(p.x) + (int64_t)b * p.x_bs + (int64_t)t0 * HP;
-    auto prefetch = [&](int h) {
-        const T *xh = xbase + h * P;
+    const float res = (p.flags & 1u) ? 1.f : 0.f;
+    T *ychunk = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)t0 * HP;
+    F pend[2][PT];          // previous head's rounded outputs, stored one iteration later
+    int hprev = -1;
+
+    for (int h = h0, it = 0; h < h1; ++h, ++it) {
+        unsigned char *buf = smem + (Cfg::DB ? (it & 1) * Buf::BYTES : 0);
+        __builtin_amdgcn_s_waitcnt(0);        // this head's DMA (and older stores) complete
+        __builtin_amdgcn_s_barrier();         // ... for every wave; the other buffer is free
+        if (Cfg::DB && h + 1 < h1) issue(h + 1, smem + ((it + 1) & 1) * Buf::BYTES);
+        if (hprev >= 0) {                     // previous head's outputs
+            T *yh = ychunk + hprev * P;
 #pragma unroll
-        for (int k = 0; k < Cfg::XBT; ++k) {
-            const int blk = tid + k * THREADS;
-            if (blk < Cfg::XB) {
-                const int jb = blk / (P / 4), pb = blk % (P / 4);
-                scan_load_block<T, RJ>(xh, HP, jb * RJ, pb * 4, Qc, xr[k]);
-            }
-        }
-        const uint4 *sv = reinterpret_cast<const uint4 *>(
-            reinterpret_cast<const T *>(p.b_in) + (((int64_t)b * p.nc + c) * p.H + h) * PN);
+            for (int ri = 0; ri < 2; ++ri) {
+                const int i = (ri ? I1 : I0) * 16 + col;
+                if (i < Qc) {
 #pragma unroll
-        for (int k = 0; k < Cfg::SVT; ++k) {
-            const int v = tid + k * THREADS;
-            if (v < Cfg::SV) sr[k] = sv[v];
-        }
-        const S *cu = reinterpret_cast<const S *>(p.dA_cum) + (((int64_t)b * p.H + h) * p.nc + c) * Q;
-#pragma unroll
-        for (int k = 0; k < Cfg::CT; ++k) {
-            const int v = tid + k * THREADS;
-            if (v < Q) cr[k] = cu[v];
-        }
-    };
-    auto stage = [&](unsigned char *buf) {
-        T *xt = reinterpret_cast<T *>(buf);
-        uint4 *st = reinterpret_cast<uint4 *>(buf + Cfg::XT_BYTES);
-        S *cm = reinterpret_cast<S *>(buf + Cfg::XT_BYTES + Cfg::ST_BYTES);
-#pragma unroll
-        for (int k = 0; k < Cfg::XBT; ++k) {
-            const int blk = tid + k * THREADS;
-            if (blk < Cfg::XB) {
-                const int jb = blk / (P / 4), pb = blk % (P / 4);
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    F colv[RJ / 4];
-#pragma unroll
-                    for (int i = 0; i < RJ; ++i) colv[i / 4][i % 4] = xr[k][i][cc];
-#pragma unroll
-                    for (int q = 0; q < RJ / 4; ++q)
-                        *reinterpret_cast<F *>(xt + (pb * 4 + cc) * RS + jb * RJ + 4 * q) = colv[q];
+                    for (int pt = 0; pt < PT; ++pt)
+                        *reinterpret_cast<F *>(yh + (int64_t)i * HP + pt * 16 + g4) = pend[ri][pt];
                 }
             }
         }
-#pragma unroll
-        for (int k = 0; k < Cfg::SVT; ++k) {
-            const int v = tid + k * THREADS;
-            if (v < Cfg::SV) st[v] = sr[k];
-        }
-#pragma unroll
-        for (int k = 0; k < Cfg::CT; ++k) {
-            const int v = tid + k * THREADS;
-            if (v < Q) cm[v] = cr[k];
-        }
-    };
-    prefetch(h0);
 
-    // ---- S^T tiles of the wave's causal slots: slot s <= w is (I0, J = s); slot w + 1 is
-    // a zero pad; slot s >= w + 2 is (I1, J = s - w - 2).
-    f32x4 sT[NSLOT];
-#pragma unroll
-    for (int s = 0; s < NSLOT; ++s) {
-        sT[s] = zero_frag<f32x4>();
-        if (s == w + 1) continue;
-        const bool first = s <= w;
-        const int I = first ? I0 : I1;
-        const int J = first ? s : s - w - 2;
-        const int j = J * 16 + col;
-        const T *brow = Bb + (int64_t)j * bcp + g4;
-        const bool jv = j < Qc;
-#pragma unroll
-        for (int nt = 0; nt < NT; nt += (sizeof(T) == 2 ? 2 : 1)) {
-            if constexpr (sizeof(T) == 2) {
-                const F b0 = jv ? *reinterpret_cast<const F *>(brow + nt * 16) : zero_frag<F>();
-                const F b1 = jv ? *reinterpret_cast<const F *>(brow + (nt + 1) * 16) : zero_frag<F>();
-                const F c0 = first ? cf[0][nt] : cf[1][nt];
-                const F c1 = first ? cf[0][nt + 1] : cf[1][nt + 1];
-                sT[s] = mma_pair(b0, c0, b1, c1, sT[s]);
-            } else {
-                const F b0 = jv ? *reinterpret_cast<const F *>(brow + nt * 16) : zero_frag<F>();
-                const F c0 = first ? cf[0][nt] : cf[1][nt];
-                sT[s] = mma_one(b0, c0, sT[s]);
-            }
-        }
-        if (J == I) {   // causal mask on the diagonal tile: keep j <= i
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (g4 + r > col) sT[s][r] = 0.f;
-        }
-    }
-
-    const bool residual = (p.flags & 1u) != 0;
-    T *ybase = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)t0 * HP;
-
-    for (int h = h0, it = 0; h < h1; ++h, ++it) {
-        unsigned char *buf = smem + ((Cfg::DB && (it & 1)) ? Cfg::BUF_BYTES : 0);
-        if (!Cfg::DB && it > 0) __syncthreads();   // previous head's readers are done
-        stage(buf);
-        if (h + 1 < h1) prefetch(h + 1);
-        __syncthreads();
-
-        const T *xt = reinterpret_cast<const T *>(buf);
-        const T *stb = reinterpret_cast<const T *>(buf + Cfg::XT_BYTES);
-        const S *cm = reinterpret_cast<const S *>(buf + Cfg::XT_BYTES + Cfg::ST_BYTES);
-        const float Dh = p.D ? p.D[h] : 0.f;
-
-        // Z = C b(c-1)^T, then scale row i by exp(cum_i)
+        const float dres = (p.D ? p.D[h] : 0.f) + res;
         f32x4 acc[2][PT];
+        switch (w) {   // uniform: every wave runs the body specialised for its own index
+#define SSD_W(WW) case WW: if constexpr (WW < NW) scan_head<T, Q, P, N, WW>(buf, sT, cf, dres, lane, acc); break;
+            SSD_W(0) SSD_W(1) SSD_W(2) SSD_W(3) SSD_W(4) SSD_W(5) SSD_W(6) SSD_W(7)
+#undef SSD_W
+            default: break;
+        }
 #pragma unroll
         for (int ri = 0; ri < 2; ++ri)
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[ri][pt] = zero_frag<f32x4>();
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-#pragma unroll
-            for (int nt = 0; nt < NT; nt += (sizeof(T) == 2 ? 2 : 1)) {
-                const F s0 = *reinterpret_cast<const F *>(stb + ((nt * PT + pt) * 64 + lane) * 4);
-                if constexpr (sizeof(T) == 2) {
-                    const F s1 = *reinterpret_cast<const F *>(stb + (((nt + 1) * PT + pt) * 64 + lane) * 4);
-#pragma unroll
-                    for (int ri = 0; ri < 2; ++ri)
-                        acc[ri][pt] = mma_pair(cf[ri][nt], s0, cf[ri][nt + 1], s1, acc[ri][pt]);
-                } else {
-#pragma unroll
-                    for (int ri = 0; ri < 2; ++ri) acc[ri][pt] = mma_one(cf[ri][nt], s0, acc[ri][pt]);
-                }
-            }
+            for (int pt = 0; pt < PT; ++pt) pend[ri][pt] = frag_from_f32<T>(acc[ri][pt]);
+        hprev = h;
+        if (!Cfg::DB && h + 1 < h1) {         // single buffer: refill after every wave is done
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();
+            issue(h + 1, smem);
         }
+    }
+    // last head's outputs
+    if (hprev >= 0) {
+        T *yh = ychunk + hprev * P;
 #pragma unroll
         for (int ri = 0; ri < 2; ++ri) {
-            const int ib = (ri ? I1 : I0) * 16 + g4;
+            const int i = (ri ? I1 : I0) * 16 + col;
+            if (i < Qc) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = __expf((float)cm[ib + r]);
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc[ri][pt][r] *= e;
+                for (int pt = 0; pt < PT; ++pt)
+                    *reinterpret_cast<F *>(yh + (int64_t)i * HP + pt * 16 + g4) = pend[ri][pt];
             }
         }
-
-        // by_intra: pairs of slots, each pair feeding one of the two row blocks
-        const S ci0 = cm[I0 * 16 + col], ci1 = cm[I1 * 16 + col];
-#pragma unroll
-        for (int q = 0; q < Cfg::NPAIR; ++q) {
-            F a[2];
-            int Jx[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int s = 2 * q + u;
-                if (s == w + 1) {
-                    a[u] = zero_frag<F>();
-                    Jx[u] = 0;
-                    continue;
-                }
-                const bool first = s <= w;
-                const int I = first ? I0 : I1;
-                const int J = first ? s : s - w - 2;
-                const S ci = first ? ci0 : ci1;
-                Jx[u] = J;
-                f32x4 m;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool valid = (J < I) || (g4 + r <= col);
-                    m[r] = valid ? sT[s][r] * __expf((float)(ci - cm[J * 16 + g4 + r])) : 0.f;
-                }
-                a[u] = frag_from_f32<T>(m);
-            }
-            const bool owner1 = (2 * q) >= (w + 1);
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const T *xrow = xt + (pt * 16 + col) * RS + g4;
-                const F x0 = *reinterpret_cast<const F *>(xrow + Jx[0] * 16);
-                const F x1 = *reinterpret_cast<const F *>(xrow + Jx[1] * 16);
-                if (owner1) acc[1][pt] = mma_pair(a[0], x0, a[1], x1, acc[1][pt]);
-                else acc[0][pt] = mma_pair(a[0], x0, a[1], x1, acc[0][pt]);
-            }
-        }
-
-        // epilogue: + D x (+ x), round, store
-        T *yh = ybase + h * P;
-#pragma unroll
-        for (int ri = 0; ri < 2; ++ri) {
-            const int I = ri ? I1 : I0;
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const F xv = *reinterpret_cast<const F *>(xt + (pt * 16 + col) * RS + I * 16 + g4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = I * 16 + g4 + r;
-                    const float xf = to_f32(xv[r]);
-                    float v = acc[ri][pt][r] + Dh * xf;
-                    if (residual) v += xf;
-                    if (i < Qc) yh[(int64_t)i * HP + pt * 16 + col] = from_f32<T>(v);
-                }
-            }
-        }
-        // (double buffering: the next head stages into the other buffer; its barrier
-        //  orders this head's reads before that buffer is written again)
     }
 }
 
@@ -325,6 +513,18 @@ static hipError_t launch_scan_t(const Problem &p, hipStream_t s) {
     }
 }
 
+template <typename T, int Q, int N>
+static hipError_t launch_cb_t(const Problem &p, hipStream_t s) {
+    using Cfg = ScanCfg<T, Q, 16, N>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)chunk_cb_kernel<T, Q, N>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::CB_LDS);
+    if (attr != hipSuccess) return attr;
+    const int64_t nblk = (int64_t)p.batch * p.nc * p.G;
+    if (nblk <= 0 || nblk > 0x7fffffff) return hipErrorInvalidValue;
+    chunk_cb_kernel<T, Q, N><<<(unsigned)nblk, Cfg::THREADS, Cfg::CB_LDS, s>>>(p);
+    return hipGetLastError();
+}
+
 #define SSD_SCAN_SHAPES(X, T)                                                              \
     X(T, 64, 16, 16) X(T, 64, 16, 32) X(T, 64, 16, 64) X(T, 64, 16, 128)                   \
     X(T, 64, 32, 32) X(T, 64, 32, 64) X(T, 64, 32, 128) X(T, 64, 64, 64) X(T, 64, 64, 128) \
@@ -336,6 +536,15 @@ static hipError_t launch_scan_t(const Problem &p, hipStream_t s) {
     if (p.Q == q && p.P == pp && p.N == nn) return launch_scan_t<T, q, pp, nn>(p, s);
 #define SSD_SCAN_OK(T, q, pp, nn) \
     if (Q == q && P == pp && N == nn) return ScanCfg<T, q, pp, nn>::OK;
+
+#define SSD_CB_CASE(T, q, pp, nn) \
+    if (p.Q == q && p.N == nn) return launch_cb_t<T, q, nn>(p, s);
+
+hipError_t launch_chunk_cb(const Problem &p, hipStream_t s) {
+    if (p.dtype == 1) { SSD_SCAN_SHAPES(SSD_CB_CASE, bf16) }
+    else { SSD_SCAN_SHAPES(SSD_CB_CASE, float) }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_chunk_scan(const Problem &p, hipStream_t s) {
     if (p.dtype == 1) { SSD_SCAN_SHAPES(SSD_SCAN_CASE, bf16) }

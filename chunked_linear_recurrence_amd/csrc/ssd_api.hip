@@ -6,7 +6,7 @@
 // [分块推理 §2.1] (intra-chunk parts from a zero state), [分块推理 §2.2] (state pass and
 // the by_inter correction) and, for the layer stack, [分块推理 §3.2] (vertical segments
 // with a per-layer state store).
-#include "../../include/libssdscan.h"
+#include "libssdscan.h"
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -37,10 +37,11 @@ ssd_status_t ok() {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kStages = 5;   // chunk_cumsum, chunk_state, state_pass, chunk_cb, chunk_scan
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t dA, bintra, bin, total;
+    size_t dA, bintra, bin, cb, decF, decG, total;
 };
 
 int64_t act_bytes(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
@@ -67,6 +68,17 @@ bool layout_for(const ssd_dims_t &d, int64_t L, int32_t Q, Layout *lo) {
     off += align_up((size_t)states * 4);
     lo->bin = off;
     off += align_up((size_t)states * act_bytes(d.dtype));
+    // causal C.B^T tiles: (Q/16)(Q/16 + 1)/2 tiles of 256 values per (batch, chunk, group)
+    int64_t cbn;
+    const int64_t nrb = Q / 16;
+    if (!mul_ok(d.batch * nc, d.ngroups, lim, &cbn) || !mul_ok(cbn, nrb * (nrb + 1) / 2 * 256, lim, &cbn))
+        return false;
+    lo->cb = off;
+    off += align_up((size_t)cbn * 4);
+    lo->decF = off;
+    off += align_up((size_t)t * 4);
+    lo->decG = off;
+    off += align_up((size_t)t * 4);
     lo->total = off;
     return true;
 }
@@ -147,7 +159,7 @@ ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q) {
     const int64_t units = d.batch * p.nc * d.ngroups;
     const int64_t hpg = d.nheads / d.ngroups;
     p.heads_per_wg_state = heads_per_wg(units, hpg, 1024, "SSD_HEADS_PER_WG_STATE");
-    p.heads_per_wg_scan = heads_per_wg(units, hpg, 2048, "SSD_HEADS_PER_WG_SCAN");
+    p.heads_per_wg_scan = heads_per_wg(units, hpg, 512, "SSD_HEADS_PER_WG_SCAN");
     return p;
 }
 
@@ -160,7 +172,9 @@ ssd_status_t run_layer(const ssd::Problem &p, hipStream_t s, int first_stage, in
         return fail(SSD_ERR_HIP, "chunk_state launch failed: %s", hipGetErrorString(e));
     if (in(3) && (e = ssd::launch_state_pass(p, s)) != hipSuccess)
         return fail(SSD_ERR_HIP, "state_pass launch failed: %s", hipGetErrorString(e));
-    if (in(4) && (e = ssd::launch_chunk_scan(p, s)) != hipSuccess)
+    if (in(4) && (e = ssd::launch_chunk_cb(p, s)) != hipSuccess)
+        return fail(SSD_ERR_HIP, "chunk_cb launch failed: %s", hipGetErrorString(e));
+    if (in(5) && (e = ssd::launch_chunk_scan(p, s)) != hipSuccess)
         return fail(SSD_ERR_HIP, "chunk_scan launch failed: %s", hipGetErrorString(e));
     return SSD_OK;
 }
@@ -211,6 +225,9 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     p.dA_cum = ws + lo.dA;
     p.b_intra = reinterpret_cast<float *>(ws + lo.bintra);
     p.b_in = ws + lo.bin;
+    p.cb = ws + lo.cb;
+    p.decF = reinterpret_cast<float *>(ws + lo.decF);
+    p.decG = reinterpret_cast<float *>(ws + lo.decG);
     st = run_layer(p, static_cast<hipStream_t>(stream), first_stage, last_stage);
     return st == SSD_OK ? ok() : st;
 }
@@ -238,7 +255,7 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, const void *x, const voi
                                 int32_t chunk_Q, void *y, float *final_state, uint32_t flags,
                                 void *workspace, size_t workspace_bytes, void *stream) {
     return fwd_impl(dims, x, dt, A, B, C, D, init_state, chunk_Q, y, final_state, flags, workspace,
-                    workspace_bytes, stream, 1, 4);
+                    workspace_bytes, stream, 1, kStages);
 }
 
 ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const void *dt, const float *A,
@@ -246,13 +263,13 @@ ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const 
                                    int32_t chunk_Q, void *y, float *final_state, uint32_t flags,
                                    void *workspace, size_t workspace_bytes, void *stream,
                                    int32_t first_stage, int32_t last_stage) {
-    if (first_stage < 1 || last_stage > 4 || first_stage > last_stage)
-        return fail(SSD_ERR_BAD_SHAPE, "stages must satisfy 1 <= first_stage <= last_stage <= 4");
+    if (first_stage < 1 || last_stage > kStages || first_stage > last_stage)
+        return fail(SSD_ERR_BAD_SHAPE, "stages must satisfy 1 <= first_stage <= last_stage <= %d", kStages);
     return fwd_impl(dims, x, dt, A, B, C, D, init_state, chunk_Q, y, final_state, flags, workspace,
                     workspace_bytes, stream, first_stage, last_stage);
 }
 
-ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_t offsets[4]) {
+ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_t offsets[5]) {
     ssd_status_t st = check_dims(dims, chunk_Q);
     if (st != SSD_OK) return st;
     if (!offsets) return fail(SSD_ERR_NULL_ARG, "offsets is NULL");
@@ -261,7 +278,8 @@ ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_
     offsets[0] = lo.dA;
     offsets[1] = lo.bintra;
     offsets[2] = lo.bin;
-    offsets[3] = lo.total;
+    offsets[3] = lo.cb;
+    offsets[4] = lo.total;
     return ok();
 }
 
@@ -356,7 +374,10 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
             p.dA_cum = lws + lo.dA;
             p.b_intra = reinterpret_cast<float *>(lws + lo.bintra);
             p.b_in = lws + lo.bin;
-            st = run_layer(p, s, 1, 4);
+            p.cb = lws + lo.cb;
+            p.decF = reinterpret_cast<float *>(lws + lo.decF);
+            p.decG = reinterpret_cast<float *>(lws + lo.decG);
+            st = run_layer(p, s, 1, kStages);
             if (st != SSD_OK) return st;
         }
     }

@@ -45,8 +45,11 @@ struct Problem {
     float *final_state;                      // [batch, H, P, N] or null
     uint32_t flags;
     void *dA_cum;      // [batch, H, nc, Q] of CumT<act>
+    float *decF;       // [batch, H, nc, Q] exp(cum[end of 16-token block] - cum[i])
+    float *decG;       // [batch, H, nc, Q] exp(cum[i])
     float *b_intra;    // [batch, nc, H, P*N] tile order
     void *b_in;        // [batch, nc, H, P*N] tile order, act dtype
+    void *cb;          // [batch, nc, G, causal tiles, 256] C.B^T tiles, float32
     int heads_per_wg_state;   // head group of chunk_state
     int heads_per_wg_scan;    // head group of chunk_scan
 };
@@ -54,6 +57,7 @@ struct Problem {
 hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_state(const Problem &p, hipStream_t s);
 hipError_t launch_state_pass(const Problem &p, hipStream_t s);
+hipError_t launch_chunk_cb(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_scan(const Problem &p, hipStream_t s);
 bool chunk_state_supported(int dtype, int Q, int P, int N);
 bool chunk_scan_supported(int dtype, int Q, int P, int N);

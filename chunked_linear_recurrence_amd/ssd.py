@@ -109,8 +109,11 @@ def segmented_workspace_bytes(dims, chunk, V) -> int:
     return lib().ssd_segmented_workspace_bytes(ctypes.byref(dims), chunk, V)
 
 
+NSTAGES = 5   # chunk_cumsum, chunk_state, state_pass, chunk_cb, chunk_scan
+
+
 def workspace_layout(dims, chunk):
-    offs = (ctypes.c_size_t * 4)()
+    offs = (ctypes.c_size_t * 5)()
     _check(lib().ssd_workspace_layout(ctypes.byref(dims), chunk, offs))
     return list(offs)
 
@@ -120,7 +123,7 @@ def alloc_workspace(nbytes, device):
 
 
 def fwd(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y=None, final_state=None,
-        residual=False, workspace=None, stream=None, want_final=True, first_stage=1, last_stage=4):
+        residual=False, workspace=None, stream=None, want_final=True, first_stage=1, last_stage=NSTAGES):
     """One layer over the whole sequence (ssd_chunk_scan_fwd).  Returns (y, final_state)."""
     dims = dims_of(x, B)
     nbytes = workspace_bytes(dims, chunk)
@@ -137,7 +140,7 @@ def fwd(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y=None, final_sta
     flags = SSD_FLAG_RESIDUAL if residual else 0
     args = (ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
             chunk, _ptr(y), _ptr(final_state), flags, _ptr(workspace), workspace.numel(), _stream(stream))
-    if first_stage == 1 and last_stage == 4:
+    if first_stage == 1 and last_stage == NSTAGES:
         _check(lib().ssd_chunk_scan_fwd(*args))
     else:
         _check(lib().ssd_chunk_scan_stages(*args, first_stage, last_stage))
