@@ -49,7 +49,10 @@ struct ScanCfg {
     static constexpr int HEAD_BYTES = Q * P * (int)sizeof(T) + P * N * (int)sizeof(T) +
                                       Q * (int)sizeof(typename CumT<T>::type) + 2 * Q * 4;
     static constexpr bool DB = 2 * HEAD_BYTES <= kLdsBytes;     // double-buffered head data
-    static constexpr int LDS = DB ? 2 * HEAD_BYTES : HEAD_BYTES;
+    static constexpr int YPIECES = P * (int)sizeof(T) / 16;      // 16-byte pieces per output row
+    static constexpr int YW = 32 * P * (int)sizeof(T);           // one wave's staged outputs
+    static constexpr bool YS = DB && 2 * HEAD_BYTES + NW * YW <= kLdsBytes;
+    static constexpr int LDS = (DB ? 2 * HEAD_BYTES : HEAD_BYTES) + (YS ? NW * YW : 0);
     static constexpr int CB_LDS = Q * BROW * (int)sizeof(T);
     static constexpr bool OK = LDS <= kLdsBytes && CB_LDS <= kLdsBytes &&
                                (sizeof(T) == 4 || NT % 2 == 0) && (Q == 64 || Q == 128 || Q == 256) &&
@@ -226,11 +229,14 @@ struct HeadBuf {
 };
 
 // Per-head products of wave W (all slot choices and offsets are compile-time):
-// Z^T scaled by G, the decayed S^T tiles times x^T, and (D + res) x.
-template <typename T, int Q, int P, int N, int W>
+// Z^T scaled by G, the decayed S^T tiles times x^T, and (D + res) x.  hook(k) is called
+// at 1 + PT + NPAIR fixed points of the body (k known at compile time once unrolled);
+// the caller uses it to spread its memory traffic through the matrix-core work.
+template <typename T, int Q, int P, int N, int W, typename Hook>
 __device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 (&sT)[ScanCfg<T, Q, P, N>::NSLOT],
                                       const typename TF<T>::type (&cf)[2][ScanCfg<T, Q, P, N>::NT],
-                                      float dres, int lane, f32x4 (&acc)[2][ScanCfg<T, Q, P, N>::PT]) {
+                                      float dres, int lane, f32x4 (&acc)[2][ScanCfg<T, Q, P, N>::PT],
+                                      Hook &&hook) {
     using Cfg = ScanCfg<T, Q, P, N>;
     using Buf = HeadBuf<T, Q, P, N>;
     using F = typename TF<T>::type;
@@ -252,6 +258,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 
     for (int ri = 0; ri < 2; ++ri)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[ri][pt] = zero_frag<f32x4>();
+    hook(0);
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
 #pragma unroll
@@ -267,6 +274,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 
                 for (int ri = 0; ri < 2; ++ri) acc[ri][pt] = mma_one(s0, cf[ri][nt], acc[ri][pt]);
             }
         }
+        hook(1 + pt);
     }
     const S ci0 = cm[I0 * 16 + col], ci1 = cm[I1 * 16 + col];
     {
@@ -312,6 +320,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 
             if (owner1) acc[1][pt] = mma_pair(x0, a[0], x1, a[1], acc[1][pt]);
             else acc[0][pt] = mma_pair(x0, a[0], x1, a[1], acc[0][pt]);
         }
+        hook(1 + PT + q);
     }
 
     // + (D + residual) x on the matrix cores: B operand diag(D + res) split into a high
@@ -337,6 +346,12 @@ __device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 
     }
 }
 
+// Staged outputs of one wave: 32 rows (its two row blocks) of YPIECES 16-byte pieces;
+// piece q of row r sits at position q ^ ysw(r), so the fragment writes and the row reads
+// both spread over all banks.
+template <int YPIECES>
+__device__ __forceinline__ int ysw(int r) { return r & ((YPIECES < 8 ? YPIECES : 8) - 1); }
+
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_kernel(Problem p) {
     using Cfg = ScanCfg<T, Q, P, N>;
@@ -345,8 +360,17 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     typedef typename CumT<T>::type S;
     constexpr int THREADS = Cfg::THREADS, NW = Cfg::NW;
     constexpr int NRB = Cfg::NRB, NSLOT = Cfg::NSLOT, PT = Cfg::PT, NT = Cfg::NT;
-    constexpr int NSTEP = sizeof(T) == 2 ? 2 : 1;
     constexpr int XPIECES = P * (int)sizeof(T) / 16;          // 16-byte pieces per x row
+    constexpr int YPIECES = Cfg::YPIECES;
+    // memory work per head and wave, in single-instruction items:
+    constexpr int XK = (Q * XPIECES + THREADS - 1) / THREADS;           // x tile
+    constexpr int SP = Buf::ST / 16, SK = (SP + THREADS - 1) / THREADS;  // b_in state
+    constexpr int CP = Buf::CM / 16, FP = Buf::FG / 16;                  // cum, F, G
+    constexpr int NDMA = XK + SK + 1;
+    constexpr int NSTQ = 32 * YPIECES / 64;                               // staged-output stores
+    constexpr int NHOOK = 1 + PT + Cfg::NPAIR;
+    constexpr int NITEM = NDMA + (Cfg::YS ? NSTQ : 0);
+    static_assert(NSTQ * 64 == 32 * YPIECES, "output rows must fill whole store instructions");
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -369,50 +393,57 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     const int64_t bcp = (int64_t)p.G * N;
     const int I0 = w, I1 = NRB - 1 - w;
 
-    // ---- per-lane byte offsets of this thread's DMA pieces (same for every head)
-    constexpr int XK = (Q * XPIECES + THREADS - 1) / THREADS;
-    int xoff[XK];
-#pragma unroll
-    for (int k = 0; k < XK; ++k) {
-        const int piece = (k * NW + w) * 64 + lane;            // LDS piece written by this lane
-        const int r = piece / XPIECES, qp = piece % XPIECES;
-        const int q = qp ^ (sizeof(T) == 2 ? x_swz<XPIECES>(r) : 0);
-        const int rr = min(r, Qc - 1);                          // rows past a short chunk repeat the last
-        xoff[k] = (rr * HP) * (int)sizeof(T) + q * 16;
-    }
     const unsigned char *xchunk = reinterpret_cast<const unsigned char *>(p.x) +
                                   ((int64_t)b * p.x_bs + (int64_t)t0 * HP) * (int64_t)sizeof(T);
-    auto issue = [&](int h, unsigned char *buf) {
-        const unsigned char *xh = xchunk + (int64_t)h * P * sizeof(T);
-#pragma unroll
-        for (int k = 0; k < XK; ++k)
-            if ((k * NW + w) * 64 + lane < Q * XPIECES)
-                dma16(xh + xoff[k], buf + (k * NW + w) * 1024);
-        const unsigned char *sv = reinterpret_cast<const unsigned char *>(p.b_in) +
-                                  (((int64_t)b * p.nc + c) * p.H + h) * PN * (int64_t)sizeof(T);
-        constexpr int SP = Buf::ST / 16;
-#pragma unroll
-        for (int k = 0; k < (SP + THREADS - 1) / THREADS; ++k)
-            if ((k * NW + w) * 64 + lane < SP)
-                dma16(sv + ((k * NW + w) * 64 + lane) * 16, buf + Buf::O_ST + (k * NW + w) * 1024);
-        const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
-        const unsigned char *cs = reinterpret_cast<const unsigned char *>(reinterpret_cast<const S *>(p.dA_cum) + tok);
-        constexpr int CP = Buf::CM / 16;
-#pragma unroll
-        for (int k = 0; k < (CP + THREADS - 1) / THREADS; ++k)
-            if ((k * NW + w) * 64 + lane < CP)
-                dma16(cs + ((k * NW + w) * 64 + lane) * 16, buf + Buf::O_CM + (k * NW + w) * 1024);
-        constexpr int FP = Buf::FG / 16;
-        const unsigned char *fs = reinterpret_cast<const unsigned char *>(p.decF + tok);
-        const unsigned char *gs = reinterpret_cast<const unsigned char *>(p.decG + tok);
-#pragma unroll
-        for (int k = 0; k < (FP + THREADS - 1) / THREADS; ++k)
-            if ((k * NW + w) * 64 + lane < FP) {
-                dma16(fs + ((k * NW + w) * 64 + lane) * 16, buf + Buf::O_F + (k * NW + w) * 1024);
-                dma16(gs + ((k * NW + w) * 64 + lane) * 16, buf + Buf::O_G + (k * NW + w) * 1024);
+    // DMA item k of head h into buffer buf: x pieces, then b_in pieces, then cum/F/G.
+    // Lane l of the wave fills LDS bytes [16 l, 16 l + 16) of the item's 1 KB block.
+    auto dma_item = [&](int k, int h, unsigned char *buf) {
+        if (k < XK) {
+            const int piece = (k * NW + w) * 64 + lane;
+            if ((k * NW + w) * 64 < Q * XPIECES) {              // uniform (Q * XPIECES % 64 == 0)
+                const int r = piece / XPIECES, qp = piece % XPIECES;
+                const int q = qp ^ (sizeof(T) == 2 ? x_swz<XPIECES>(r) : 0);
+                const int rr = min(r, Qc - 1);                  // rows past a short chunk repeat the last
+                dma16(xchunk + ((int64_t)rr * HP + (int64_t)h * P) * (int64_t)sizeof(T) + q * 16,
+                      buf + (k * NW + w) * 1024);
             }
+        } else if (k < XK + SK) {
+            const int kk = k - XK;
+            if ((kk * NW + w) * 64 < SP) {
+                const unsigned char *sv = reinterpret_cast<const unsigned char *>(p.b_in) +
+                                          (((int64_t)b * p.nc + c) * p.H + h) * PN * (int64_t)sizeof(T);
+                dma16(sv + ((kk * NW + w) * 64 + lane) * 16, buf + Buf::O_ST + (kk * NW + w) * 1024);
+            }
+        } else {
+            const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
+            if (w * 64 < CP)
+                dma16(reinterpret_cast<const unsigned char *>(reinterpret_cast<const S *>(p.dA_cum) + tok) +
+                          (w * 64 + lane) * 16, buf + Buf::O_CM + w * 1024);
+            if (w * 64 < FP) {
+                dma16(reinterpret_cast<const unsigned char *>(p.decF + tok) + (w * 64 + lane) * 16,
+                      buf + Buf::O_F + w * 1024);
+                dma16(reinterpret_cast<const unsigned char *>(p.decG + tok) + (w * 64 + lane) * 16,
+                      buf + Buf::O_G + w * 1024);
+            }
+        }
     };
-    issue(h0, smem);
+    static_assert(CP <= THREADS && FP <= THREADS, "cum/F/G fit one DMA item");
+
+    T *ychunk = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)t0 * HP;
+    unsigned char *ys = smem + (Cfg::DB ? 2 : 1) * Buf::BYTES + (Cfg::YS ? w * Cfg::YW : 0);
+    // Store item k of head hs: 64 pieces of this wave's staged rows, 16 bytes per lane,
+    // whole output rows per group of YPIECES lanes.
+    auto store_item = [&](int k, int hs) {
+        const int pc = k * 64 + lane;
+        const int row = pc / YPIECES, q = pc % YPIECES;
+        const int i = (row < 16 ? I0 : I1) * 16 + (row & 15);
+        const uint4 v = *reinterpret_cast<const uint4 *>(ys + (row * YPIECES + (q ^ ysw<YPIECES>(row))) * 16);
+        if (i < Qc)
+            *reinterpret_cast<uint4 *>(ychunk + (int64_t)i * HP + (int64_t)hs * P + q * (16 / (int)sizeof(T))) = v;
+    };
+
+#pragma unroll
+    for (int k = 0; k < NDMA; ++k) dma_item(k, h0, smem);
 
     // ---- per workgroup: this wave's S^T tiles (float) and C fragments
     f32x4 sT[NSLOT];
@@ -439,59 +470,65 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     }
 
     const float res = (p.flags & 1u) ? 1.f : 0.f;
-    T *ychunk = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)t0 * HP;
-    F pend[2][PT];          // previous head's rounded outputs, stored one iteration later
-    int hprev = -1;
-
     for (int h = h0, it = 0; h < h1; ++h, ++it) {
         unsigned char *buf = smem + (Cfg::DB ? (it & 1) * Buf::BYTES : 0);
+        unsigned char *nbuf = smem + (Cfg::DB ? ((it + 1) & 1) * Buf::BYTES : 0);
         __builtin_amdgcn_s_waitcnt(0);        // this head's DMA (and older stores) complete
         __builtin_amdgcn_s_barrier();         // ... for every wave; the other buffer is free
-        if (Cfg::DB && h + 1 < h1) issue(h + 1, smem + ((it + 1) & 1) * Buf::BYTES);
-        if (hprev >= 0) {                     // previous head's outputs
-            T *yh = ychunk + hprev * P;
+        const bool more = h + 1 < h1;
+        // Item k: the next head's DMA (double buffer), then the previous head's staged stores.
+        auto hook = [&](int k) {
+            if (k < NDMA) {
+                if (Cfg::DB && more) dma_item(k, h + 1, nbuf);
+            } else if (k < NITEM) {
+                if (Cfg::YS && h > h0) store_item(k - NDMA, h - 1);
+            }
+        };
+        const float dres = (p.D ? p.D[h] : 0.f) + res;
+        f32x4 acc[2][PT];
+        switch (w) {   // uniform: every wave runs the body specialised for its own index
+#define SSD_W(WW) case WW: if constexpr (WW < NW) scan_head<T, Q, P, N, WW>(buf, sT, cf, dres, lane, acc, hook); break;
+            SSD_W(0) SSD_W(1) SSD_W(2) SSD_W(3) SSD_W(4) SSD_W(5) SSD_W(6) SSD_W(7)
+#undef SSD_W
+            default: break;
+        }
+#pragma unroll
+        for (int k = NHOOK; k < NITEM; ++k) hook(k);   // items the body had no room for
+
+        if constexpr (Cfg::YS) {
+            // rounded outputs into this wave's staging rows; stored during the next head
+#pragma unroll
+            for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const int row = ri * 16 + col;
+                    const int byte = (pt * 16 + g4) * (int)sizeof(T);
+                    const int q = (byte >> 4) ^ ysw<YPIECES>(row);
+                    *reinterpret_cast<F *>(ys + (row * YPIECES + q) * 16 + (byte & 15)) =
+                        frag_from_f32<T>(acc[ri][pt]);
+                }
+        } else {
+            T *yh = ychunk + h * P;
 #pragma unroll
             for (int ri = 0; ri < 2; ++ri) {
                 const int i = (ri ? I1 : I0) * 16 + col;
                 if (i < Qc) {
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt)
-                        *reinterpret_cast<F *>(yh + (int64_t)i * HP + pt * 16 + g4) = pend[ri][pt];
+                        *reinterpret_cast<F *>(yh + (int64_t)i * HP + pt * 16 + g4) = frag_from_f32<T>(acc[ri][pt]);
                 }
             }
         }
-
-        const float dres = (p.D ? p.D[h] : 0.f) + res;
-        f32x4 acc[2][PT];
-        switch (w) {   // uniform: every wave runs the body specialised for its own index
-#define SSD_W(WW) case WW: if constexpr (WW < NW) scan_head<T, Q, P, N, WW>(buf, sT, cf, dres, lane, acc); break;
-            SSD_W(0) SSD_W(1) SSD_W(2) SSD_W(3) SSD_W(4) SSD_W(5) SSD_W(6) SSD_W(7)
-#undef SSD_W
-            default: break;
-        }
-#pragma unroll
-        for (int ri = 0; ri < 2; ++ri)
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) pend[ri][pt] = frag_from_f32<T>(acc[ri][pt]);
-        hprev = h;
-        if (!Cfg::DB && h + 1 < h1) {         // single buffer: refill after every wave is done
+        if (!Cfg::DB && more) {               // single buffer: refill after every wave is done
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
-            issue(h + 1, smem);
+#pragma unroll
+            for (int k = 0; k < NDMA; ++k) dma_item(k, h + 1, smem);
         }
     }
-    // last head's outputs
-    if (hprev >= 0) {
-        T *yh = ychunk + hprev * P;
+    if constexpr (Cfg::YS) {                  // last head's staged outputs (own rows: no barrier)
 #pragma unroll
-        for (int ri = 0; ri < 2; ++ri) {
-            const int i = (ri ? I1 : I0) * 16 + col;
-            if (i < Qc) {
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    *reinterpret_cast<F *>(yh + (int64_t)i * HP + pt * 16 + g4) = pend[ri][pt];
-            }
-        }
+        for (int k = 0; k < NSTQ; ++k) store_item(k, h1 - 1);
     }
 }
 
