@@ -229,11 +229,16 @@ struct HeadBuf {
 };
 
 // Per-head products of wave W (all slot choices and offsets are compile-time):
-// Z^T scaled by G, the decayed S^T tiles times x^T, and (D + res) x.  hook(k) is called
-// at 1 + PT + NPAIR fixed points of the body (k known at compile time once unrolled);
-// the caller uses it to spread its memory traffic through the matrix-core work.
+// Z^T scaled by G, the decayed S^T tiles times x^T, and (D + res) x.  hook(k, nbuf, ys)
+// is called at 1 + PT + NPAIR fixed points of the body (k known at compile time once
+// unrolled); the caller uses it to spread its memory traffic through the matrix-core
+// work.  buf (this head's inputs), nbuf (the next head's, being filled by DMA) and ys
+// (staged outputs) are disjoint LDS regions; saying so (restrict) lets the compiler
+// keep this head's LDS reads from waiting on the next head's DMA.
 template <typename T, int Q, int P, int N, int W, typename Hook>
-__device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 (&sT)[ScanCfg<T, Q, P, N>::NSLOT],
+__device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf, unsigned char *__restrict__ nbuf,
+                                      unsigned char *__restrict__ ys,
+                                      const f32x4 (&sT)[ScanCfg<T, Q, P, N>::NSLOT],
                                       const typename TF<T>::type (&cf)[2][ScanCfg<T, Q, P, N>::NT],
                                       float dres, int lane, f32x4 (&acc)[2][ScanCfg<T, Q, P, N>::PT],
                                       Hook &&hook) {
@@ -258,7 +263,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 
     for (int ri = 0; ri < 2; ++ri)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[ri][pt] = zero_frag<f32x4>();
-    hook(0);
+    hook(0, nbuf, ys);
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
 #pragma unroll
@@ -274,7 +279,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 
                 for (int ri = 0; ri < 2; ++ri) acc[ri][pt] = mma_one(s0, cf[ri][nt], acc[ri][pt]);
             }
         }
-        hook(1 + pt);
+        hook(1 + pt, nbuf, ys);
     }
     const S ci0 = cm[I0 * 16 + col], ci1 = cm[I1 * 16 + col];
     {
@@ -320,7 +325,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *buf, const f32x4 
             if (owner1) acc[1][pt] = mma_pair(x0, a[0], x1, a[1], acc[1][pt]);
             else acc[0][pt] = mma_pair(x0, a[0], x1, a[1], acc[0][pt]);
         }
-        hook(1 + PT + q);
+        hook(1 + PT + q, nbuf, ys);
     }
 
     // + (D + residual) x on the matrix cores: B operand diag(D + res) split into a high
@@ -433,7 +438,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     unsigned char *ys = smem + (Cfg::DB ? 2 : 1) * Buf::BYTES + (Cfg::YS ? w * Cfg::YW : 0);
     // Store item k of head hs: 64 pieces of this wave's staged rows, 16 bytes per lane,
     // whole output rows per group of YPIECES lanes.
-    auto store_item = [&](int k, int hs) {
+    auto store_item = [&](int k, int hs, const unsigned char *ys) {
         const int pc = k * 64 + lane;
         const int row = pc / YPIECES, q = pc % YPIECES;
         const int i = (row < 16 ? I0 : I1) * 16 + (row & 15);
@@ -477,23 +482,23 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         __builtin_amdgcn_s_barrier();         // ... for every wave; the other buffer is free
         const bool more = h + 1 < h1;
         // Item k: the next head's DMA (double buffer), then the previous head's staged stores.
-        auto hook = [&](int k) {
+        auto hook = [&](int k, unsigned char *nb, const unsigned char *yst) {
             if (k < NDMA) {
-                if (Cfg::DB && more) dma_item(k, h + 1, nbuf);
+                if (Cfg::DB && more) dma_item(k, h + 1, nb);
             } else if (k < NITEM) {
-                if (Cfg::YS && h > h0) store_item(k - NDMA, h - 1);
+                if (Cfg::YS && h > h0) store_item(k - NDMA, h - 1, yst);
             }
         };
         const float dres = (p.D ? p.D[h] : 0.f) + res;
         f32x4 acc[2][PT];
         switch (w) {   // uniform: every wave runs the body specialised for its own index
-#define SSD_W(WW) case WW: if constexpr (WW < NW) scan_head<T, Q, P, N, WW>(buf, sT, cf, dres, lane, acc, hook); break;
+#define SSD_W(WW) case WW: if constexpr (WW < NW) scan_head<T, Q, P, N, WW>(buf, nbuf, ys, sT, cf, dres, lane, acc, hook); break;
             SSD_W(0) SSD_W(1) SSD_W(2) SSD_W(3) SSD_W(4) SSD_W(5) SSD_W(6) SSD_W(7)
 #undef SSD_W
             default: break;
         }
 #pragma unroll
-        for (int k = NHOOK; k < NITEM; ++k) hook(k);   // items the body had no room for
+        for (int k = NHOOK; k < NITEM; ++k) hook(k, nbuf, ys);   // items the body had no room for
 
         if constexpr (Cfg::YS) {
             // rounded outputs into this wave's staging rows; stored during the next head
@@ -528,7 +533,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     }
     if constexpr (Cfg::YS) {                  // last head's staged outputs (own rows: no barrier)
 #pragma unroll
-        for (int k = 0; k < NSTQ; ++k) store_item(k, h1 - 1);
+        for (int k = 0; k < NSTQ; ++k) store_item(k, h1 - 1, ys);
     }
 }
 
