@@ -15,8 +15,8 @@ Besides the headline tokens/s the line carries:
   cpu_baseline  the fp64 CPU oracle timed on this host's cores on the same inputs.
 
 Algorithmic bytes count every input a kernel needs once and every output it must write
-once, in the dtype the library stores it in (activations bf16, decays and local states
-float32, states entering a chunk bf16).
+once, in the dtype the library stores it in (activations and the per-chunk states b_intra
+and b_in in the activation dtype; decay sums, init and final states float32).
 """
 import argparse
 import json
@@ -62,12 +62,12 @@ def alg_bytes(w):
     cbt = b * nc * G * nrb * (nrb + 1) // 2 * 256 * e   # causal C.B^T tiles
     k = {
         "chunk_cumsum": dt + cum,
-        "chunk_state": x + bc + cum + states * 4,
-        "state_pass": states * 4 + states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
+        "chunk_state": x + bc + cum + states * e,
+        "state_pass": 2 * states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
         "chunk_cb": 2 * bc + cbt,
         "chunk_scan": x + bc + cum + states * e + cbt + y,
     }
-    method = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final + 2 * states * 4 + 2 * states * e
+    method = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final + 4 * states * e
     return k, method
 
 

@@ -13,7 +13,8 @@
 // keeps its A-operand fragments (its share of the n rows, all Q tokens) in registers for
 // all heads of the group.  Per head, x is scaled by w in fp32, rounded to the activation
 // dtype, transposed into LDS (double-buffered), and read as B-operand fragments; the
-// result tiles are stored in tile order as one float4 per lane (coalesced 1 KiB per wave).
+// result tiles are rounded once to the activation dtype and stored in tile order, 4
+// values per lane (coalesced 512 B or 1 KiB per wave).
 // The next head's x rows and decays are loaded into registers before the current head's
 // products start, so HBM latency overlaps the matrix work.
 #include "ssd_common.h"
@@ -175,13 +176,13 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_k
                     acc[i][pt] = mma_pair(af[i][kt], x0, af[i][kt + 1], x1, acc[i][pt]);
             }
         }
-        float *out = p.b_intra + (((int64_t)b * p.nc + c) * p.H + h) * PN;
+        T *out = reinterpret_cast<T *>(p.b_intra) + (((int64_t)b * p.nc + c) * p.H + h) * PN;
 #pragma unroll
         for (int i = 0; i < Cfg::NTW; ++i) {
             const int nt = wave * Cfg::NTW + i;
 #pragma unroll
             for (int pt = 0; pt < Cfg::PT; ++pt)
-                *reinterpret_cast<f32x4 *>(out + ((nt * Cfg::PT + pt) * 64 + lane) * 4) = acc[i][pt];
+                *reinterpret_cast<F *>(out + ((nt * Cfg::PT + pt) * 64 + lane) * 4) = frag_from_f32<T>(acc[i][pt]);
         }
     }
 }

@@ -65,7 +65,7 @@ bool layout_for(const ssd_dims_t &d, int64_t L, int32_t Q, Layout *lo) {
     lo->dA = off;
     off += align_up((size_t)t * (d.dtype == SSD_F32 ? 8 : 4));
     lo->bintra = off;
-    off += align_up((size_t)states * 4);
+    off += align_up((size_t)states * act_bytes(d.dtype));
     lo->bin = off;
     off += align_up((size_t)states * act_bytes(d.dtype));
     // causal C.B^T tiles: (Q/16)(Q/16 + 1)/2 tiles of 256 values per (batch, chunk, group)
@@ -223,7 +223,7 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     p.flags = flags;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     p.dA_cum = ws + lo.dA;
-    p.b_intra = reinterpret_cast<float *>(ws + lo.bintra);
+    p.b_intra = ws + lo.bintra;
     p.b_in = ws + lo.bin;
     p.cb = ws + lo.cb;
     p.decF = reinterpret_cast<float *>(ws + lo.decF);
@@ -372,7 +372,7 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
             p.final_state = layer_states + (size_t)l * state_elems;
             p.flags = flags;
             p.dA_cum = lws + lo.dA;
-            p.b_intra = reinterpret_cast<float *>(lws + lo.bintra);
+            p.b_intra = lws + lo.bintra;
             p.b_in = lws + lo.bin;
             p.cb = lws + lo.cb;
             p.decF = reinterpret_cast<float *>(lws + lo.decF);

@@ -47,7 +47,7 @@ struct Problem {
     void *dA_cum;      // [batch, H, nc, Q] of CumT<act>
     float *decF;       // [batch, H, nc, Q] exp(cum[end of 16-token block] - cum[i])
     float *decG;       // [batch, H, nc, Q] exp(cum[i])
-    float *b_intra;    // [batch, nc, H, P*N] tile order
+    void *b_intra;     // [batch, nc, H, P*N] act dtype, tile order
     void *b_in;        // [batch, nc, H, P*N] tile order, act dtype
     void *cb;          // [batch, nc, G, causal tiles, 256] C.B^T tiles, float32
     int heads_per_wg_state;   // head group of chunk_state

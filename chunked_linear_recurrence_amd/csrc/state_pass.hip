@@ -3,16 +3,17 @@
 //
 //     b(-1) = init_state (or 0),   b(c) = b_intra(c) + exp(dA_cum[c, last]) * b(c-1)
 //
-// It writes b_in[c] = b(c-1), the state entering chunk c (in the activation dtype, which
-// is what chunk_scan's matrix cores consume), and final_state = b(nc-1) in float32.
-// The carried state stays in float32 registers for the whole pass.
+// It writes b_in[c] = b(c-1), the state entering chunk c, and final_state = b(nc-1) in
+// float32.  b_intra and b_in are stored in the activation dtype (what chunk_scan's matrix
+// cores consume); the carried state b stays in float32 registers for the whole pass, so
+// only the per-chunk terms are rounded, never the running sum.
 //
 // The recurrence is elementwise over the P x N state, so the state of one (batch, head)
-// is split across workgroups of one wave, each owning 256 elements (a float4 per lane),
-// giving batch * H * P * N / 256 independent waves.  The loads of b_intra for the next
-// kSP chunks do not depend on the carried state, so they are issued a whole group ahead
-// of the dependent multiply-adds; the pass is a pure HBM stream (read 4 bytes, write act
-// bytes per state element per chunk).
+// is split across workgroups of one wave, each owning 256 elements (4 per lane), giving
+// batch * H * P * N / 256 independent waves.  The loads of b_intra do not depend on the
+// carried state, so they run two groups of K chunks ahead of the dependent multiply-adds
+// (K loads of the next group are in flight while the current group is consumed); the pass
+// is a pure HBM stream (read and write act bytes per state element per chunk).
 //
 // b_intra and b_in use the tile order of the other kernels (see libssdscan.h); only
 // init_state / final_state use the row-major [P][N] order, so the thread owning tile
@@ -20,8 +21,6 @@
 #include "ssd_common.h"
 
 namespace ssd {
-
-constexpr int kSP = 8;   // chunks whose loads are in flight together
 
 template <typename T>
 __device__ __forceinline__ void store_state(T *dst, const float4 &v);
@@ -36,14 +35,22 @@ __device__ __forceinline__ void store_state<bf16>(bf16 *dst, const float4 &v) {
     *reinterpret_cast<bf16x4 *>(dst) = o;
 }
 
+__device__ __forceinline__ float4 as_float4(const f32x4 &v) { return make_float4(v[0], v[1], v[2], v[3]); }
+__device__ __forceinline__ float4 as_float4(const bf16x4 &v) {
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
 __device__ __forceinline__ float4 fma4(float a, const float4 &s, const float4 &b) {
     return make_float4(fmaf(a, s.x, b.x), fmaf(a, s.y, b.y), fmaf(a, s.z, b.z), fmaf(a, s.w, b.w));
 }
 
 template <typename T>
 __global__ __launch_bounds__(64) void state_pass_kernel(Problem p) {
+    typedef typename TF<T>::type V;
+    typedef typename CumT<T>::type S;
+    constexpr int K = sizeof(T) == 2 ? 16 : 8;         // chunks per load group
     const int PN = p.P * p.N;
-    const int e4 = blockIdx.x * 64 + threadIdx.x;        // float4 index within one state
+    const int e4 = blockIdx.x * 64 + threadIdx.x;        // 4-element group within one state
     const int h = blockIdx.y, b = blockIdx.z;
     if (e4 * 4 >= PN) return;
     const int e = e4 * 4;
@@ -57,31 +64,35 @@ __global__ __launch_bounds__(64) void state_pass_kernel(Problem p) {
     if (p.init) s = *reinterpret_cast<const float4 *>(p.init + std_off);
 
     const int64_t cstride = (int64_t)p.H * PN;            // between chunks
-    const float *bi = p.b_intra + ((int64_t)b * p.nc * p.H + h) * PN + e;
+    const T *bi = reinterpret_cast<const T *>(p.b_intra) + ((int64_t)b * p.nc * p.H + h) * PN + e;
     T *bo = reinterpret_cast<T *>(p.b_in) + ((int64_t)b * p.nc * p.H + h) * PN + e;
-    typedef typename CumT<T>::type S;
     const S *cum = reinterpret_cast<const S *>(p.dA_cum) + ((int64_t)b * p.H + h) * p.nc * p.Q + (p.Q - 1);
+    const int nc = p.nc;
 
-    int c = 0;
-    for (; c + kSP <= p.nc; c += kSP) {
-        float4 v[kSP];
-        S d[kSP];
+    V va[K], vb[K];
+    S da[K], db[K];
+    auto load = [&](int c0, V (&v)[K], S (&d)[K]) {
 #pragma unroll
-        for (int u = 0; u < kSP; ++u) {
-            v[u] = *reinterpret_cast<const float4 *>(bi + (c + u) * cstride);
-            d[u] = cum[(int64_t)(c + u) * p.Q];
-        }
+        for (int u = 0; u < K; ++u)
+            if (c0 + u < nc) {                               // uniform
+                v[u] = *reinterpret_cast<const V *>(bi + (int64_t)(c0 + u) * cstride);
+                d[u] = cum[(int64_t)(c0 + u) * p.Q];
+            }
+    };
+    auto consume = [&](int c0, const V (&v)[K], const S (&d)[K]) {
 #pragma unroll
-        for (int u = 0; u < kSP; ++u) {
-            store_state<T>(bo + (c + u) * cstride, s);
-            s = fma4(expf((float)d[u]), s, v[u]);
-        }
-    }
-    for (; c < p.nc; ++c) {
-        const float4 v = *reinterpret_cast<const float4 *>(bi + c * cstride);
-        const S d = cum[(int64_t)c * p.Q];
-        store_state<T>(bo + c * cstride, s);
-        s = fma4(expf((float)d), s, v);
+        for (int u = 0; u < K; ++u)
+            if (c0 + u < nc) {
+                store_state<T>(bo + (int64_t)(c0 + u) * cstride, s);
+                s = fma4(expf((float)d[u]), s, as_float4(v[u]));
+            }
+    };
+    load(0, va, da);
+    for (int c = 0; c < nc; c += 2 * K) {
+        load(c + K, vb, db);
+        consume(c, va, da);
+        load(c + 2 * K, va, da);
+        consume(c + K, vb, db);
     }
     if (p.final_state) *reinterpret_cast<float4 *>(p.final_state + std_off) = s;
 }

@@ -77,7 +77,9 @@ typedef enum ssd_status {
 typedef enum ssd_dtype {
     SSD_F32 = 0,   /* activations stored and computed in float32 (fp32 matrix cores)        */
     SSD_BF16 = 1   /* activations stored in bfloat16, products on bf16 matrix cores, fp32
-                      accumulation; states and decays always float32                         */
+                      accumulation.  The state carried across chunks is summed in float32;
+                      the per-chunk states stored in the workspace (b_intra, b_in) are
+                      rounded to bfloat16; decays, init_state and final_state are float32 */
 } ssd_dtype_t;
 
 typedef struct ssd_dims {
@@ -96,7 +98,7 @@ typedef struct ssd_dims {
 
 /* Size in bytes of the workspace ssd_chunk_scan_fwd needs for these dims and chunk_Q,
  * or 0 when the arguments are invalid.  The workspace holds the per-chunk log-decay
- * prefix sums, two per-chunk state buffers (nheads * headdim * dstate * (4 + act bytes) /
+ * prefix sums, two per-chunk state buffers (nheads * headdim * dstate * 2 * act bytes /
  * chunk_Q bytes per token), the per-chunk C.B^T tiles ((chunk_Q + 16) / 2 * ngroups * 4 bytes
  * per token) and two float32 decay factors per token and head. */
 size_t ssd_chunk_scan_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q);
@@ -167,7 +169,7 @@ ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const 
  *               for SSD_BF16 activations: sum of dt*A from the
  *               chunk start to each token, inclusive (past a short last chunk: the chunk
  *               total);
- *   offsets[1]  b_intra  float32, per (batch, chunk, head) a P x N state in tile order;
+ *   offsets[1]  b_intra  act dtype, per (batch, chunk, head) a P x N state in tile order;
  *   offsets[2]  b_in     act dtype, the state entering each chunk, same tile order;
  *   offsets[3]  cb       float32, per (batch, chunk, group) the causal 16x16 tiles of
  *               S^T = B_c C_c^T (tile (I, J), J <= I, at index I(I+1)/2 + J; lane l, value r

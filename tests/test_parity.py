@@ -67,10 +67,10 @@ def test_stages_match_oracle_intermediates(dtype):
     # past the short last chunk: the chunk total
     qlast = L - (nc - 1) * Q
     assert np.allclose(cum[:, :, -1, qlast:], cum[:, :, -1, qlast - 1:qlast], rtol=0, atol=0)
-    bint = ws[offs[1]:offs[1] + b * nc * H * P * N * 4].view(torch.float32)
-    bint = as_np(ssd.tile_order_to_pn(bint.reshape(b, nc, H, P * N), P, N))
     e = 4 if dtype == "f32" else 2
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    bint = ws[offs[1]:offs[1] + b * nc * H * P * N * e].view(tdt)
+    bint = as_np(ssd.tile_order_to_pn(bint.reshape(b, nc, H, P * N), P, N))
     bin_ = ws[offs[2]:offs[2] + b * nc * H * P * N * e].view(tdt)
     bin_ = as_np(ssd.tile_order_to_pn(bin_.reshape(b, nc, H, P * N), P, N))
     err = err_for(dtype)
