@@ -3,14 +3,15 @@
 A step is one ssd_chunk_scan_fwd call (all five kernels: chunk_cumsum, chunk_state,
 state_pass, chunk_cb, chunk_scan) over the whole batch of the 128K-token workload
 (long_context_b1_L131072_h48: batch 1, L 131072, H 48, P 64, N 128, Q 256, bf16), with
-every input already resident in HBM.  W untimed warm-up steps, then exactly K timed
-steps between two device synchronisations.
+every input already resident in HBM.  Untimed: steps repeated for --settle-ms (clock
+ramp-up), then W warm-up steps; then exactly K timed steps between two device
+synchronisations.
 
 Besides the headline tokens/s the line carries:
   roofline      the dominant kernel's achieved HBM rate (algorithmic bytes per launch /
                 its mean duration, from HIP events around each launch on the stream it
-                runs on) against the 8 TB/s peak;
-  kernels       the same figures for all four kernels, plus matrix-core rates;
+                runs on, inside full steps) against the 8 TB/s peak;
+  kernels       the same figures for all five kernels, plus matrix-core rates;
   end_to_end    the method's bytes / step time against peak HBM bandwidth;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores on the same inputs.
 
@@ -36,6 +37,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed: repeat the step for this long before the warm-up steps, so the "
+                         "timed steps start at steady clocks (the per-step time falls by about 20%% over "
+                         "the first ~20 ms of load); 0 disables")
     ap.add_argument("--workload", default=None, help="workload name (default: the 128K-token layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=0, help="launches per kernel for per-kernel timing "
@@ -127,6 +132,11 @@ def main():
         ssd.fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["init_state"], w.chunk, y=y,
                 final_state=fin, workspace=ws, stream=stream, first_stage=first, last_stage=last)
 
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -144,21 +154,23 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     tokens_per_s = w.tokens / (ms_step * 1e-3)
 
-    # per-kernel durations: HIP events around each single-kernel launch on the same stream
+    # per-kernel durations: full steps again, the five stages launched one by one in order
+    # on the same stream with a HIP event between consecutive kernels, so each kernel is
+    # timed where it runs inside a step (after its producer, before its consumer).
     names = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_cb", "chunk_scan"]
     kb, method_bytes = alg_bytes(w)
     kf = alg_flops(w)
     ksteps = args.kernel_steps or args.steps
-    kernels = {}
-    for stage, name in enumerate(names, start=1):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(ksteps)]
-        for a, b_ in evs:
-            a.record(stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(ksteps)]
+    for row in evs:
+        row[0].record(stream)
+        for stage in range(1, len(names) + 1):
             step(stage, stage)
-            b_.record(stream)
-        torch.cuda.synchronize()
-        us = sum(a.elapsed_time(b_) for a, b_ in evs) / ksteps * 1e3
+            row[stage].record(stream)
+    torch.cuda.synchronize()
+    kernels = {}
+    for k, name in enumerate(names):
+        us = sum(row[k].elapsed_time(row[k + 1]) for row in evs) / ksteps * 1e3
         gbs = kb[name] / (us * 1e-6) / 1e9
         rec = {"us": round(us, 2), "alg_bytes": kb[name], "GB_s": round(gbs, 1),
                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -167,6 +179,7 @@ def main():
             rec.update({"alg_flops": kf[name], "TFLOP_s": round(tf, 2),
                         "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
         kernels[name] = rec
+    staged_ms = sum(row[0].elapsed_time(row[-1]) for row in evs) / ksteps
     torch.cuda.synchronize()
     dom = max(names, key=lambda n: kernels[n]["us"])
     roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB_s"], "peak": HBM_PEAK_GBS,
@@ -186,6 +199,7 @@ def main():
         "end_to_end": {"method_bytes": method_bytes, "GB_s": round(e2e_gbs, 1),
                        "hbm_frac": round(e2e_gbs / HBM_PEAK_GBS, 4)},
         "kernels": kernels,
+        "ms_per_step_staged": round(staged_ms, 4),
         "wall_s_timed": round(wall, 4),
     }
     if args.copy_calibration:
