@@ -51,7 +51,9 @@ def parse():
 
 
 def alg_bytes(w):
-    """Algorithmic bytes per launch of each kernel and of the whole method."""
+    """Bytes each kernel must move once per launch (every input it reads and every output
+    it writes, once, in the dtype the library stores it), and the method's bytes: the
+    compulsory activations and states plus the per-chunk state exchange."""
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     e = w.act_bytes
     nc = w.nchunks
@@ -60,17 +62,18 @@ def alg_bytes(w):
     y = x
     dt = b * L * H * e
     bc = b * L * G * N * e                      # one of B or C
-    cum = b * H * nc * Q * cum_e
+    cum = b * H * nc * Q * cum_e                # dA_cum
+    fg = 2 * b * H * nc * Q * 4                 # the two float32 decay factors per token-head
     states = b * nc * H * P * N
     init = final = b * H * P * N * 4
     nrb = Q // 16
-    cbt = b * nc * G * nrb * (nrb + 1) // 2 * 256 * e   # causal C.B^T tiles
+    cbt = b * nc * G * nrb * (nrb + 1) // 2 * 256 * 4   # causal C.B^T tiles, float32
     k = {
-        "chunk_cumsum": dt + cum,
+        "chunk_cumsum": dt + cum + fg,
         "chunk_state": x + bc + cum + states * e,
         "state_pass": 2 * states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
         "chunk_cb": 2 * bc + cbt,
-        "chunk_scan": x + bc + cum + states * e + cbt + y,
+        "chunk_scan": x + bc + cum + fg + states * e + cbt + y,
     }
     method = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final + 4 * states * e
     return k, method
@@ -84,6 +87,33 @@ def alg_flops(w):
     per_chunk_cb = G * Q * (Q + 1) * N
     return {"chunk_state": b * nc * per_chunk_state, "chunk_cb": b * nc * per_chunk_cb,
             "chunk_scan": b * nc * per_chunk_scan}
+
+
+def kernel_sources_sha256():
+    """sha256 over the HIP sources of the library (file names and contents, sorted)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "chunked_linear_recurrence_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary (scaled by its copy calibration), or None when there is none for this workload
+    or the kernel sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha256") != kernel_sources_sha256() or kernel not in t.get("kernels", {}):
+        return None
+    return t["kernels"][kernel]["bytes"]
 
 
 def cpu_baseline(d, w):
@@ -183,7 +213,7 @@ def main():
     torch.cuda.synchronize()
     dom = max(names, key=lambda n: kernels[n]["us"])
     roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GB_s"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kernels[dom]["hbm_frac"], "traffic": None,
+            "unit": "GB/s", "frac": kernels[dom]["hbm_frac"], "traffic": measured_traffic(w.name, dom),
             "alg_bytes_per_launch": kb[dom], "mean_launch_us": kernels[dom]["us"]}
     e2e_gbs = method_bytes / (ms_step * 1e-3) / 1e9
 
