@@ -1,7 +1,7 @@
 """Throughput of the chunked SSD scan on one MI355X, as one JSON line.
 
-A step is one ssd_chunk_scan_fwd call (all five kernels: chunk_cumsum, chunk_state,
-state_pass, chunk_cb, chunk_scan) over the whole batch of the 128K-token workload
+A step is one ssd_chunk_scan_fwd call (all four kernels: chunk_cumsum, chunk_state,
+state_pass, chunk_scan) over the whole batch of the 128K-token workload
 (long_context_b1_L131072_h48: batch 1, L 131072, H 48, P 64, N 128, Q 256, bf16), with
 every input already resident in HBM.  Untimed: steps repeated for --settle-ms (clock
 ramp-up), then W warm-up steps; then exactly K timed steps between two device
@@ -11,7 +11,7 @@ Besides the headline tokens/s the line carries:
   roofline      the dominant kernel's achieved HBM rate (algorithmic bytes per launch /
                 its mean duration, from HIP events around each launch on the stream it
                 runs on, inside full steps) against the 8 TB/s peak;
-  kernels       the same figures for all five kernels, plus matrix-core rates;
+  kernels       the same figures for all four kernels, plus matrix-core rates;
   end_to_end    the method's bytes / step time against peak HBM bandwidth;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores on the same inputs.
 
@@ -66,14 +66,11 @@ def alg_bytes(w):
     fg = 2 * b * H * nc * Q * 4                 # the two float32 decay factors per token-head
     states = b * nc * H * P * N
     init = final = b * H * P * N * 4
-    nrb = Q // 16
-    cbt = b * nc * G * nrb * (nrb + 1) // 2 * 256 * 4   # causal C.B^T tiles, float32
     k = {
         "chunk_cumsum": dt + cum + fg,
         "chunk_state": x + bc + cum + states * e,
         "state_pass": 2 * states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
-        "chunk_cb": 2 * bc + cbt,
-        "chunk_scan": x + bc + cum + fg + states * e + cbt + y,
+        "chunk_scan": x + 2 * bc + cum + fg + states * e + y,
     }
     method = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final + 4 * states * e
     return k, method
@@ -84,9 +81,8 @@ def alg_flops(w):
     nc = w.nchunks
     per_chunk_state = H * 2 * Q * N * P
     per_chunk_scan = H * (Q * (Q + 1) * P + 2 * Q * N * P)
-    per_chunk_cb = G * Q * (Q + 1) * N
-    return {"chunk_state": b * nc * per_chunk_state, "chunk_cb": b * nc * per_chunk_cb,
-            "chunk_scan": b * nc * per_chunk_scan}
+    per_chunk_cb = G * Q * (Q + 1) * N          # causal C.B^T, once per chunk and group
+    return {"chunk_state": b * nc * per_chunk_state, "chunk_scan": b * nc * (per_chunk_scan + per_chunk_cb)}
 
 
 def kernel_sources_sha256():
@@ -184,10 +180,10 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     tokens_per_s = w.tokens / (ms_step * 1e-3)
 
-    # per-kernel durations: full steps again, the five stages launched one by one in order
+    # per-kernel durations: full steps again, the four stages launched one by one in order
     # on the same stream with a HIP event between consecutive kernels, so each kernel is
     # timed where it runs inside a step (after its producer, before its consumer).
-    names = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_cb", "chunk_scan"]
+    names = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_scan"]
     kb, method_bytes = alg_bytes(w)
     kf = alg_flops(w)
     ksteps = args.kernel_steps or args.steps

@@ -1,4 +1,4 @@
-// chunk_cb and chunk_scan: every chunk's output, [分块推理 §2.1-§2.2] of the page
+// chunk_scan: every chunk's output, [分块推理 §2.1-§2.2] of the page
 // "分块推理：解锁循环模型并行计算，实现长序列高效处理":
 //
 //   by_intra_i = sum_{j <= i} (C_i . B_j) exp(cum_i - cum_j) x_j      (zero-state intra part)
@@ -8,23 +8,24 @@
 // rounded once to the activation dtype.  cum is the chunk's dA_cum row and b(c-1) is
 // b_in[c] from state_pass.
 //
-// Both kernels cut a chunk into Q/16 row blocks of 16 tokens and use Q/32 waves; wave w
-// owns row blocks I0 = w and I1 = Q/16-1-w, so every wave has the same number (Q/16 + 1)
-// of causal 16x16 tiles (J <= I).  The wave's tile list ("slots") is: slot s <= w is
+// One workgroup per (batch, chunk, group of heads that read the same B and C).  A chunk
+// is cut into Q/16 row blocks of 16 tokens and the workgroup has Q/32 waves; wave w owns
+// row blocks I0 = w and I1 = Q/16-1-w, so every wave has the same number (Q/16 + 1) of
+// causal 16x16 tiles (J <= I).  The wave's tile list ("slots") is: slot s <= w is
 // (I0, J = s), slot w + 1 is a zero pad, slot s >= w + 2 is (I1, J = s - w - 2); the pad
 // keeps pairs of slots inside one row block.  The wave index is read as a scalar, so
 // every choice that depends on it is a uniform branch.
 //
-// chunk_cb (once per chunk and B/C group, shared by all heads of the group):
-//   S^T = B_c C_c^T on the matrix cores for the causal tiles, zero above the diagonal,
-//   stored in the operand dtype in tile order: tile (I, J) at index I(I+1)/2 + J, lane
-//   (col, g) value r holding S^T[16J + 4g + r][16I + col].
-// chunk_scan (one workgroup per chunk and head):
-//   x is transposed into LDS (tokens contiguous per channel), b_in copied, and three
-//   per-token factors computed once:  cum_j,  F_j = exp(cum_end(j) - cum_j),
-//   G_j = exp(cum_j), where end(j) is the last token of j's 16-token block.  The products
-//   are computed transposed (y^T[p][i]) so that a lane's 4 accumulator values are 4
-//   consecutive channels of one token and leave as one 8-byte store:
+// Once per workgroup, each wave computes its causal tiles of S^T = B_c C_c^T on the
+// matrix cores (B fragments straight from L2, C fragments kept in registers), zero above
+// the diagonal, and keeps them in fp32 registers for every head of the group: C.B^T is
+// formed once per chunk and group, never per head.
+//
+// Per head, x is brought into LDS by DMA (tokens x channels, read back as transposed
+// fragments), b_in likewise, and three per-token factors: cum_j, F_j =
+// exp(cum_end(j) - cum_j), G_j = exp(cum_j), where end(j) is the last token of j's
+// 16-token block.  The products are computed transposed (y^T[p][i]) so that a lane's 4
+// accumulator values are 4 consecutive channels of one token:
 //     Z^T = b(c-1) C^T, column i scaled by G_i;
 //     y^T += x^T (S^T . decay), where an off-diagonal tile (J < I) factorises the decay as
 //       exp(cum_i - cum_j) = exp(cum_i - cum_end(J)) * F_j (both factors <= 1, one exp per
@@ -44,8 +45,6 @@ struct ScanCfg {
     static constexpr int NSLOT = NRB + 2, NPAIR = NSLOT / 2;
     static constexpr int NTRI = NRB * (NRB + 1) / 2;            // causal tiles per chunk
     static constexpr int PT = P / 16, NT = N / 16;
-    static constexpr int BROW = N + (sizeof(T) == 2 ? 8 : 4);    // staged B row stride (chunk_cb)
-    static constexpr int BV = Q * N * (int)sizeof(T) / 16;       // 16-byte vectors of B
     static constexpr int HEAD_BYTES = Q * P * (int)sizeof(T) + P * N * (int)sizeof(T) +
                                       Q * (int)sizeof(typename CumT<T>::type) + 2 * Q * 4;
     static constexpr bool DB = 2 * HEAD_BYTES <= kLdsBytes;     // double-buffered head data
@@ -53,8 +52,11 @@ struct ScanCfg {
     static constexpr int YW = 32 * P * (int)sizeof(T);           // one wave's staged outputs
     static constexpr bool YS = DB && 2 * HEAD_BYTES + NW * YW <= kLdsBytes;
     static constexpr int LDS = (DB ? 2 * HEAD_BYTES : HEAD_BYTES) + (YS ? NW * YW : 0);
-    static constexpr int CB_LDS = Q * BROW * (int)sizeof(T);
-    static constexpr bool OK = LDS <= kLdsBytes && CB_LDS <= kLdsBytes &&
+    // The chunk's B tile (Q x N) is staged in LDS for the S^T products when it fits beside
+    // the first head's buffer; otherwise the B fragments are loaded from L2.
+    static constexpr int BPIECES = N * (int)sizeof(T) / 16;      // 16-byte pieces per B row
+    static constexpr bool BL = DB && Q * N * (int)sizeof(T) <= LDS - HEAD_BYTES;
+    static constexpr bool OK = LDS <= kLdsBytes &&
                                (sizeof(T) == 4 || NT % 2 == 0) && (Q == 64 || Q == 128 || Q == 256) &&
                                P * (int)sizeof(T) >= 32;
 };
@@ -71,87 +73,6 @@ __device__ __forceinline__ Slot slot_of(int s, int w, int NRB) {
     r.I = r.first ? w : NRB - 1 - w;
     r.J = r.pad ? 0 : (r.first ? s : s - w - 2);
     return r;
-}
-
-// ---------------------------------------------------------------------------------
-// chunk_cb: causal S^T tiles of one (batch, chunk, group)
-// ---------------------------------------------------------------------------------
-template <typename T, int Q, int N>
-__global__ __launch_bounds__((Q / 32) * 64) void chunk_cb_kernel(Problem p) {
-    using Cfg = ScanCfg<T, Q, 16, N>;
-    using F = typename TF<T>::type;
-    constexpr int THREADS = Cfg::THREADS, BROW = Cfg::BROW, NRB = Cfg::NRB, NT = Cfg::NT;
-    constexpr int NSTEP = sizeof(T) == 2 ? 2 : 1;
-    extern __shared__ __align__(16) unsigned char smem[];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 15, g4 = 4 * (lane >> 4);
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);     // (b, c, grp)
-    const int grp = logical % p.G;
-    const int bc = logical / p.G;
-    const int c = bc % p.nc, b = bc / p.nc;
-    const int t0 = c * Q;
-    const int Qc = min(Q, p.L - t0);
-    const int64_t bcp = (int64_t)p.G * N;
-    const T *Cb = reinterpret_cast<const T *>(p.C) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
-    const T *Bb = reinterpret_cast<const T *>(p.B) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
-    const int I0 = w, I1 = NRB - 1 - w;
-
-    T *bs = reinterpret_cast<T *>(smem);
-    {
-        constexpr int VPR = N * (int)sizeof(T) / 16;
-        for (int v = tid; v < Cfg::BV; v += THREADS) {
-            const int j = v / VPR, q = v % VPR;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (j < Qc) val = *reinterpret_cast<const uint4 *>(Bb + (int64_t)j * bcp + q * (16 / (int)sizeof(T)));
-            *reinterpret_cast<uint4 *>(bs + j * BROW + q * (16 / (int)sizeof(T))) = val;
-        }
-    }
-    F cf[2][NT];
-#pragma unroll
-    for (int ri = 0; ri < 2; ++ri) {
-        const int i = (ri ? I1 : I0) * 16 + col;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            cf[ri][nt] = (i < Qc) ? *reinterpret_cast<const F *>(Cb + (int64_t)i * bcp + nt * 16 + g4)
-                                  : zero_frag<F>();
-    }
-    __syncthreads();
-
-    float *out = reinterpret_cast<float *>(p.cb) + (int64_t)logical * Cfg::NTRI * 256;
-#pragma unroll
-    for (int s = 0; s < Cfg::NSLOT; ++s) {
-        const Slot sl = slot_of(s, w, NRB);
-        if (sl.pad) continue;
-        f32x4 t = zero_frag<f32x4>();
-        const T *brow = bs + (sl.J * 16 + col) * BROW + g4;
-        if (sl.first) {
-#pragma unroll
-            for (int nt = 0; nt < NT; nt += NSTEP) {
-                if constexpr (sizeof(T) == 2)
-                    t = mma_pair(*reinterpret_cast<const F *>(brow + nt * 16), cf[0][nt],
-                                 *reinterpret_cast<const F *>(brow + (nt + 1) * 16), cf[0][nt + 1], t);
-                else
-                    t = mma_one(*reinterpret_cast<const F *>(brow + nt * 16), cf[0][nt], t);
-            }
-        } else {
-#pragma unroll
-            for (int nt = 0; nt < NT; nt += NSTEP) {
-                if constexpr (sizeof(T) == 2)
-                    t = mma_pair(*reinterpret_cast<const F *>(brow + nt * 16), cf[1][nt],
-                                 *reinterpret_cast<const F *>(brow + (nt + 1) * 16), cf[1][nt + 1], t);
-                else
-                    t = mma_one(*reinterpret_cast<const F *>(brow + nt * 16), cf[1][nt], t);
-            }
-        }
-        if (sl.J == sl.I) {                                     // uniform: diagonal tile
-#pragma unroll
-            for (int r = 0; r < 4; ++r) t[r] = (g4 + r <= col) ? t[r] : 0.f;
-        }
-        const int tri = sl.I * (sl.I + 1) / 2 + sl.J;
-        *reinterpret_cast<f32x4 *>(out + (tri * 64 + lane) * 4) = t;
-    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -450,17 +371,8 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
 #pragma unroll
     for (int k = 0; k < NDMA; ++k) dma_item(k, h0, smem);
 
-    // ---- per workgroup: this wave's S^T tiles (float) and C fragments
-    f32x4 sT[NSLOT];
-    {
-        const float *cbt = reinterpret_cast<const float *>(p.cb) + ((int64_t)bc * p.G + grp) * Cfg::NTRI * 256;
-#pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
-            const Slot sl = slot_of(s, w, NRB);
-            const int tri = sl.I * (sl.I + 1) / 2 + sl.J;
-            sT[s] = sl.pad ? zero_frag<f32x4>() : *reinterpret_cast<const f32x4 *>(cbt + (tri * 64 + lane) * 4);
-        }
-    }
+    // ---- per workgroup: this wave's C fragments, then its causal S^T = B C^T tiles
+    constexpr int NSTEP = sizeof(T) == 2 ? 2 : 1;
     F cf[2][NT];
     {
         const T *Cb = reinterpret_cast<const T *>(p.C) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
@@ -472,6 +384,72 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
                 cf[ri][nt] = (i < Qc) ? *reinterpret_cast<const F *>(Cb + (int64_t)i * bcp + nt * 16 + g4)
                                       : zero_frag<F>();
         }
+    }
+    // Tile (I, J): rows j of block J (A operand: B[j][n], lane (col, g) holding 4
+    // consecutive n), columns i of block I (B operand: the C fragments above); output
+    // lane (col, g) value r holds S^T[16J + 4g + r][16I + col].  Rows past a short chunk
+    // are zero.
+    f32x4 sT[NSLOT];
+    {
+        const T *Bb = reinterpret_cast<const T *>(p.B) + (int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N;
+        // B fragment of row j, columns n0..n0+3: from the staged tile (piece q of row j at
+        // position q ^ bsw(j), so the 16 rows read by one load hit different banks) or
+        // from L2.
+        constexpr int BMASK = (Cfg::BPIECES < 16 ? Cfg::BPIECES : 16) - 1;
+        const unsigned char *bst = smem + Buf::BYTES;
+        auto bfrag = [&](int j, int n0) -> F {
+            if (j >= Qc) return zero_frag<F>();
+            if constexpr (Cfg::BL) {
+                const int byte = n0 * (int)sizeof(T);
+                const int pos = (byte >> 4) ^ (j & BMASK);
+                return *reinterpret_cast<const F *>(bst + (j * Cfg::BPIECES + pos) * 16 + (byte & 15));
+            } else {
+                return *reinterpret_cast<const F *>(Bb + (int64_t)j * bcp + n0);
+            }
+        };
+        if constexpr (Cfg::BL) {
+            // DMA the tile (rows past a short chunk repeat the last row; bfrag zeroes them)
+            const unsigned char *bsrc = reinterpret_cast<const unsigned char *>(Bb);
+            constexpr int BK = (Q * Cfg::BPIECES + THREADS - 1) / THREADS;
+#pragma unroll
+            for (int k = 0; k < BK; ++k) {
+                if ((k * NW + w) * 64 < Q * Cfg::BPIECES) {     // uniform
+                    const int slot = (k * NW + w) * 64 + lane;
+                    const int j = slot / Cfg::BPIECES, q = (slot % Cfg::BPIECES) ^ (j & BMASK);
+                    dma16(bsrc + (int64_t)min(j, Qc - 1) * bcp * (int64_t)sizeof(T) + q * 16,
+                          smem + Buf::BYTES + (k * NW + w) * 1024);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);    // the tile (and the first head's inputs) landed
+            __builtin_amdgcn_s_barrier();
+        }
+#pragma unroll
+        for (int s = 0; s < NSLOT; ++s) {
+            const Slot sl = slot_of(s, w, NRB);
+            f32x4 t = zero_frag<f32x4>();
+            if (!sl.pad) {                                       // uniform
+                const int j = sl.J * 16 + col;
+                const int ri = sl.first ? 0 : 1;
+#pragma unroll
+                for (int nt = 0; nt < NT; nt += NSTEP) {
+                    const F a0 = bfrag(j, nt * 16 + g4);
+                    if constexpr (sizeof(T) == 2) {
+                        const F a1 = bfrag(j, (nt + 1) * 16 + g4);
+                        t = ri ? mma_pair(a0, cf[1][nt], a1, cf[1][nt + 1], t)
+                               : mma_pair(a0, cf[0][nt], a1, cf[0][nt + 1], t);
+                    } else {
+                        t = ri ? mma_one(a0, cf[1][nt], t) : mma_one(a0, cf[0][nt], t);
+                    }
+                }
+                if (sl.J == sl.I) {                              // uniform: diagonal tile
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) t[r] = (g4 + r <= col) ? t[r] : 0.f;
+                }
+            }
+            sT[s] = t;
+        }
+        // The staged tile sits in the second head buffer and the staging rows; the barrier
+        // at the top of the head loop orders these reads before the first DMA into them.
     }
 
     const float res = (p.flags & 1u) ? 1.f : 0.f;
@@ -555,18 +533,6 @@ static hipError_t launch_scan_t(const Problem &p, hipStream_t s) {
     }
 }
 
-template <typename T, int Q, int N>
-static hipError_t launch_cb_t(const Problem &p, hipStream_t s) {
-    using Cfg = ScanCfg<T, Q, 16, N>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)chunk_cb_kernel<T, Q, N>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::CB_LDS);
-    if (attr != hipSuccess) return attr;
-    const int64_t nblk = (int64_t)p.batch * p.nc * p.G;
-    if (nblk <= 0 || nblk > 0x7fffffff) return hipErrorInvalidValue;
-    chunk_cb_kernel<T, Q, N><<<(unsigned)nblk, Cfg::THREADS, Cfg::CB_LDS, s>>>(p);
-    return hipGetLastError();
-}
-
 #define SSD_SCAN_SHAPES(X, T)                                                              \
     X(T, 64, 16, 16) X(T, 64, 16, 32) X(T, 64, 16, 64) X(T, 64, 16, 128)                   \
     X(T, 64, 32, 32) X(T, 64, 32, 64) X(T, 64, 32, 128) X(T, 64, 64, 64) X(T, 64, 64, 128) \
@@ -578,15 +544,6 @@ static hipError_t launch_cb_t(const Problem &p, hipStream_t s) {
     if (p.Q == q && p.P == pp && p.N == nn) return launch_scan_t<T, q, pp, nn>(p, s);
 #define SSD_SCAN_OK(T, q, pp, nn) \
     if (Q == q && P == pp && N == nn) return ScanCfg<T, q, pp, nn>::OK;
-
-#define SSD_CB_CASE(T, q, pp, nn) \
-    if (p.Q == q && p.N == nn) return launch_cb_t<T, q, nn>(p, s);
-
-hipError_t launch_chunk_cb(const Problem &p, hipStream_t s) {
-    if (p.dtype == 1) { SSD_SCAN_SHAPES(SSD_CB_CASE, bf16) }
-    else { SSD_SCAN_SHAPES(SSD_CB_CASE, float) }
-    return hipErrorInvalidValue;
-}
 
 hipError_t launch_chunk_scan(const Problem &p, hipStream_t s) {
     if (p.dtype == 1) { SSD_SCAN_SHAPES(SSD_SCAN_CASE, bf16) }

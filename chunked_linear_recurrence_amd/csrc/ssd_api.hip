@@ -37,11 +37,11 @@ ssd_status_t ok() {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kStages = 5;   // chunk_cumsum, chunk_state, state_pass, chunk_cb, chunk_scan
+constexpr int kStages = 4;   // chunk_cumsum, chunk_state, state_pass, chunk_scan
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t dA, bintra, bin, cb, decF, decG, total;
+    size_t dA, bintra, bin, decF, decG, total;
 };
 
 int64_t act_bytes(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
@@ -68,13 +68,6 @@ bool layout_for(const ssd_dims_t &d, int64_t L, int32_t Q, Layout *lo) {
     off += align_up((size_t)states * act_bytes(d.dtype));
     lo->bin = off;
     off += align_up((size_t)states * act_bytes(d.dtype));
-    // causal C.B^T tiles: (Q/16)(Q/16 + 1)/2 tiles of 256 values per (batch, chunk, group)
-    int64_t cbn;
-    const int64_t nrb = Q / 16;
-    if (!mul_ok(d.batch * nc, d.ngroups, lim, &cbn) || !mul_ok(cbn, nrb * (nrb + 1) / 2 * 256, lim, &cbn))
-        return false;
-    lo->cb = off;
-    off += align_up((size_t)cbn * 4);
     lo->decF = off;
     off += align_up((size_t)t * 4);
     lo->decG = off;
@@ -172,9 +165,7 @@ ssd_status_t run_layer(const ssd::Problem &p, hipStream_t s, int first_stage, in
         return fail(SSD_ERR_HIP, "chunk_state launch failed: %s", hipGetErrorString(e));
     if (in(3) && (e = ssd::launch_state_pass(p, s)) != hipSuccess)
         return fail(SSD_ERR_HIP, "state_pass launch failed: %s", hipGetErrorString(e));
-    if (in(4) && (e = ssd::launch_chunk_cb(p, s)) != hipSuccess)
-        return fail(SSD_ERR_HIP, "chunk_cb launch failed: %s", hipGetErrorString(e));
-    if (in(5) && (e = ssd::launch_chunk_scan(p, s)) != hipSuccess)
+    if (in(4) && (e = ssd::launch_chunk_scan(p, s)) != hipSuccess)
         return fail(SSD_ERR_HIP, "chunk_scan launch failed: %s", hipGetErrorString(e));
     return SSD_OK;
 }
@@ -225,7 +216,6 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     p.dA_cum = ws + lo.dA;
     p.b_intra = ws + lo.bintra;
     p.b_in = ws + lo.bin;
-    p.cb = ws + lo.cb;
     p.decF = reinterpret_cast<float *>(ws + lo.decF);
     p.decG = reinterpret_cast<float *>(ws + lo.decG);
     st = run_layer(p, static_cast<hipStream_t>(stream), first_stage, last_stage);
@@ -269,7 +259,7 @@ ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const 
                     workspace_bytes, stream, first_stage, last_stage);
 }
 
-ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_t offsets[5]) {
+ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_t offsets[4]) {
     ssd_status_t st = check_dims(dims, chunk_Q);
     if (st != SSD_OK) return st;
     if (!offsets) return fail(SSD_ERR_NULL_ARG, "offsets is NULL");
@@ -278,8 +268,7 @@ ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_
     offsets[0] = lo.dA;
     offsets[1] = lo.bintra;
     offsets[2] = lo.bin;
-    offsets[3] = lo.cb;
-    offsets[4] = lo.total;
+    offsets[3] = lo.total;
     return ok();
 }
 
@@ -374,7 +363,6 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
             p.dA_cum = lws + lo.dA;
             p.b_intra = lws + lo.bintra;
             p.b_in = lws + lo.bin;
-            p.cb = lws + lo.cb;
             p.decF = reinterpret_cast<float *>(lws + lo.decF);
             p.decG = reinterpret_cast<float *>(lws + lo.decG);
             st = run_layer(p, s, 1, kStages);

@@ -49,7 +49,6 @@ struct Problem {
     float *decG;       // [batch, H, nc, Q] exp(cum[i])
     void *b_intra;     // [batch, nc, H, P*N] act dtype, tile order
     void *b_in;        // [batch, nc, H, P*N] tile order, act dtype
-    void *cb;          // [batch, nc, G, causal tiles, 256] C.B^T tiles, float32
     int heads_per_wg_state;   // head group of chunk_state
     int heads_per_wg_scan;    // head group of chunk_scan
 };
@@ -57,7 +56,6 @@ struct Problem {
 hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_state(const Problem &p, hipStream_t s);
 hipError_t launch_state_pass(const Problem &p, hipStream_t s);
-hipError_t launch_chunk_cb(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_scan(const Problem &p, hipStream_t s);
 bool chunk_state_supported(int dtype, int Q, int P, int N);
 bool chunk_scan_supported(int dtype, int Q, int P, int N);

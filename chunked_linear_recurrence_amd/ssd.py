@@ -109,11 +109,11 @@ def segmented_workspace_bytes(dims, chunk, V) -> int:
     return lib().ssd_segmented_workspace_bytes(ctypes.byref(dims), chunk, V)
 
 
-NSTAGES = 5   # chunk_cumsum, chunk_state, state_pass, chunk_cb, chunk_scan
+NSTAGES = 4   # chunk_cumsum, chunk_state, state_pass, chunk_scan
 
 
 def workspace_layout(dims, chunk):
-    offs = (ctypes.c_size_t * 5)()
+    offs = (ctypes.c_size_t * 4)()
     _check(lib().ssd_workspace_layout(ctypes.byref(dims), chunk, offs))
     return list(offs)
 

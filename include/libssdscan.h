@@ -99,8 +99,7 @@ typedef struct ssd_dims {
 /* Size in bytes of the workspace ssd_chunk_scan_fwd needs for these dims and chunk_Q,
  * or 0 when the arguments are invalid.  The workspace holds the per-chunk log-decay
  * prefix sums, two per-chunk state buffers (nheads * headdim * dstate * 2 * act bytes /
- * chunk_Q bytes per token), the per-chunk C.B^T tiles ((chunk_Q + 16) / 2 * ngroups * 4 bytes
- * per token) and two float32 decay factors per token and head. */
+ * chunk_Q bytes per token) and two float32 decay factors per token and head. */
 size_t ssd_chunk_scan_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q);
 
 /* One layer, the whole sequence [分块推理 §2-§2.2].
@@ -151,10 +150,9 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
 /* ---- inspection (tests and tools) ------------------------------------------------ */
 
 /* Runs steps first_stage..last_stage of ssd_chunk_scan_fwd (1 = log-decay prefix sums,
- * 2 = per-chunk local states, 3 = state pass, 4 = per-chunk C.B^T tiles, 5 = chunk
- * outputs) and leaves the
+ * 2 = per-chunk local states, 3 = state pass, 4 = chunk outputs) and leaves the
  * intermediates in the workspace (see ssd_workspace_layout).  A step reads what the
- * earlier steps left in the same workspace, so running 1..k and then k+1..5 with the same
+ * earlier steps left in the same workspace, so running 1..k and then k+1..4 with the same
  * arguments equals one ssd_chunk_scan_fwd call; running one step at a time is how each
  * kernel is timed on its own. */
 ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const void *dt,
@@ -171,14 +169,11 @@ ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const 
  *               total);
  *   offsets[1]  b_intra  act dtype, per (batch, chunk, head) a P x N state in tile order;
  *   offsets[2]  b_in     act dtype, the state entering each chunk, same tile order;
- *   offsets[3]  cb       float32, per (batch, chunk, group) the causal 16x16 tiles of
- *               S^T = B_c C_c^T (tile (I, J), J <= I, at index I(I+1)/2 + J; lane l, value r
- *               of a tile holds S^T[16J + 4(l/16) + r][16I + l%16]; zero above the diagonal);
- *   offsets[4]  total workspace bytes.
+ *   offsets[3]  total workspace bytes.
  * Tile order of one P x N state: 16x16 tiles indexed [n / 16][p / 16], each tile 64 lanes
  * x 4 values, where lane l, value r holds (p = 16 * (p / 16) + l % 16,
  * n = 16 * (n / 16) + 4 * (l / 16) + r). */
-ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_t offsets[5]);
+ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_t offsets[4]);
 
 /* 1 when a compiled kernel set covers (dtype, chunk_Q, headdim, dstate), else 0. */
 int32_t ssd_shape_supported(int32_t dtype, int32_t chunk_Q, int64_t headdim, int64_t dstate);

@@ -105,9 +105,7 @@ def test_workspace_sizes_and_layout():
         states = w.batch * w.nchunks * w.nheads * w.headdim * w.dstate
         assert offs[0] == 0 and offs[1] >= w.batch * w.nheads * w.nchunks * w.chunk * 4
         assert offs[2] - offs[1] >= states * e and offs[3] - offs[2] >= states * e
-        nrb = w.chunk // 16
-        assert offs[4] - offs[3] >= w.batch * w.nchunks * w.ngroups * nrb * (nrb + 1) // 2 * 256 * 4
-        assert all(o % 256 == 0 for o in offs) and nb == offs[4]
+        assert all(o % 256 == 0 for o in offs) and nb >= offs[3]
         if w.segment:
             segb = ssd.segmented_workspace_bytes(d, w.chunk, w.segment)
             # memory depends on V, not on the sequence length

@@ -52,7 +52,7 @@ def test_stages_match_oracle_intermediates(dtype):
     g = to_dev(d, DEV)
     dims = ssd.dims_of(g["x"], g["B"])
     offs = ssd.workspace_layout(dims, Q)
-    ws = torch.zeros(offs[4], dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(ssd.workspace_bytes(dims, Q), dtype=torch.uint8, device=DEV)
     ssd.fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["init_state"], Q, workspace=ws,
             last_stage=3)
     torch.cuda.synchronize()
