@@ -23,6 +23,26 @@ namespace ssd {
 
 constexpr int kCumHeads = 16;
 
+// A lane's E consecutive values as one vector store (E * sizeof(V) bytes).
+template <typename V, int E>
+__device__ __forceinline__ void store_run(V *dst, const V (&v)[E]) {
+    if constexpr (E * sizeof(V) % 16 == 0) {
+#pragma unroll
+        for (int k = 0; k < E * (int)sizeof(V) / 16; ++k) {
+            uint4 u;
+            __builtin_memcpy(&u, reinterpret_cast<const unsigned char *>(v) + 16 * k, 16);
+            reinterpret_cast<uint4 *>(dst)[k] = u;
+        }
+    } else if constexpr (E * sizeof(V) == 8) {
+        uint2 u;
+        __builtin_memcpy(&u, v, 8);
+        *reinterpret_cast<uint2 *>(dst) = u;
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[e] = v[e];
+    }
+}
+
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p) {
     typedef typename CumT<T>::type S;
@@ -69,19 +89,20 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p) {
         lastv = __shfl(lastv, last / E, 64);
         S cv[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            cv[e] = (lane * E + e <= last) ? excl + v[e] : lastv;
-            out[e] = cv[e];
-        }
+        for (int e = 0; e < E; ++e) cv[e] = (lane * E + e <= last) ? excl + v[e] : lastv;
+        store_run<S, E>(out, cv);
         // block end of this lane's tokens (E divides 16, so they share one block)
         const int src = ((lane * E) / 16 * 16 + 15) / E;
         const S cend = __shfl(cv[E - 1], src, 64);
         const int64_t fo = (((int64_t)b * p.H + hb + hh) * p.nc + c) * Q + lane * E;
+        float fv[E], gv[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            p.decF[fo + e] = expf((float)(cend - cv[e]));
-            p.decG[fo + e] = expf((float)cv[e]);
+            fv[e] = expf((float)(cend - cv[e]));
+            gv[e] = expf((float)cv[e]);
         }
+        store_run<float, E>(p.decF + fo, fv);
+        store_run<float, E>(p.decG + fo, gv);
     }
 }
 
