@@ -15,8 +15,9 @@
 // dtype, transposed into LDS (double-buffered), and read as B-operand fragments; the
 // result tiles are rounded once to the activation dtype and stored in tile order, 4
 // values per lane (coalesced 512 B or 1 KiB per wave).
-// The next head's x rows and decays are loaded into registers before the current head's
-// products start, so HBM latency overlaps the matrix work.
+// The next head's x rows and decays are loaded into registers at the start of the
+// current head (after its x is consumed, where registers are short), so their HBM
+// latency overlaps the head's work.
 #include "ssd_common.h"
 
 namespace ssd {
@@ -29,34 +30,48 @@ struct StateCfg {
     static constexpr int THREADS = NWS * 64;
     static constexpr int RS = Q + 4;                           // LDS row stride (elements)
     static constexpr int RJ = 16 / (int)sizeof(T);             // rows per transpose block
-    static constexpr int XB = (Q / RJ) * (P / 4);              // x transpose blocks
+    static constexpr int CW = 16 / (int)sizeof(T);             // columns per block (16-byte rows)
+    static constexpr int XB = (Q / RJ) * (P / CW);             // x transpose blocks
     static constexpr int XBT = (XB + THREADS - 1) / THREADS;
-    static constexpr int BB = (Q / RJ) * (N / 4);
+    static constexpr int BB = (Q / RJ) * (N / CW);
     static constexpr int BT_BYTES = N * RS * (int)sizeof(T);
     static constexpr int XW_BYTES = P * RS * (int)sizeof(T);
     static constexpr int LDS = BT_BYTES > 2 * XW_BYTES ? BT_BYTES : 2 * XW_BYTES;
+    // registers of one head's prefetched x rows and decays; when small, the next head's
+    // loads are issued at the start of the current head into a second register set (and
+    // the kernel is held to two waves per SIMD), otherwise after its x is consumed
+    static constexpr int XREGS = XBT * RJ * (16 + (int)sizeof(typename CumT<T>::type)) / 4;
+    static constexpr bool EARLY = XREGS <= 48;
+    static constexpr int WPE = EARLY ? 2 : 1;
     static constexpr bool OK = (KT % 2 == 0) && LDS <= kLdsBytes && NT % NWS == 0;
 };
 
-// Loads rows [j0, j0 + RJ) x cols [c0, c0 + 4) of a token-major tile (row pitch `pitch`
-// elements), zero past `rows`.
+// 16 bytes of one row: 8 bf16 or 4 float.
+template <typename T> struct Row16T;
+template <> struct Row16T<bf16> { typedef bf16x8 type; };
+template <> struct Row16T<float> { typedef f32x4 type; };
+
+// Loads rows [j0, j0 + RJ) x cols [c0, c0 + 16 bytes) of a token-major tile (row pitch
+// `pitch` elements), zero past `rows`.
 template <typename T, int RJ>
 __device__ __forceinline__ void load_block(const T *base, int64_t pitch, int j0, int c0, int rows,
-                                           typename TF<T>::type (&r)[RJ]) {
+                                           typename Row16T<T>::type (&r)[RJ]) {
+    typedef typename Row16T<T>::type V;
 #pragma unroll
     for (int i = 0; i < RJ; ++i) {
-        if (j0 + i < rows) r[i] = *reinterpret_cast<const typename TF<T>::type *>(base + (int64_t)(j0 + i) * pitch + c0);
-        else r[i] = zero_frag<typename TF<T>::type>();
+        if (j0 + i < rows) r[i] = *reinterpret_cast<const V *>(base + (int64_t)(j0 + i) * pitch + c0);
+        else r[i] = V{};
     }
 }
 
-// Writes the transpose of an RJ x 4 block into LDS rows c0..c0+3 at column j0, optionally
-// scaling row i by w[i] (in fp32, then rounded to T).
+// Writes the transpose of an RJ x CW block into LDS rows c0..c0+CW-1 at column j0,
+// optionally scaling row i by w[i] (in fp32, then rounded to T).
 template <typename T, int RJ, int RS, bool SCALE>
-__device__ __forceinline__ void store_block_t(T *lds, int j0, int c0, const typename TF<T>::type (&r)[RJ],
+__device__ __forceinline__ void store_block_t(T *lds, int j0, int c0, const typename Row16T<T>::type (&r)[RJ],
                                               const float *w) {
+    constexpr int CW = 16 / (int)sizeof(T);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < CW; ++cc) {
         typename TF<T>::type col[RJ / 4];
 #pragma unroll
         for (int i = 0; i < RJ; ++i) {
@@ -71,7 +86,8 @@ __device__ __forceinline__ void store_block_t(T *lds, int j0, int c0, const type
 }
 
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_kernel(Problem p) {
+__global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) __attribute__((amdgpu_waves_per_eu(StateCfg<T, Q, P, N>::WPE)))
+void chunk_state_kernel(Problem p) {
     using Cfg = StateCfg<T, Q, P, N>;
     using F = typename TF<T>::type;
     typedef typename CumT<T>::type S;
@@ -99,35 +115,41 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_k
     const T *xb = reinterpret_cast<const T *>(p.x) + (int64_t)b * p.x_bs + (int64_t)t0 * HP;
     const S *cumb = reinterpret_cast<const S *>(p.dA_cum) + ((int64_t)b * p.H) * p.nc * Q + (int64_t)c * Q;
 
-    // prefetch head h0's x rows and decays
-    F xr[Cfg::XBT][RJ];
-    S cw[Cfg::XBT][RJ];
-    S clast = 0;
-    auto prefetch = [&](int h) {
+    // x rows and decays of one head, loaded into registers one head ahead of their use
+    typedef typename Row16T<T>::type V;
+    constexpr int CW = Cfg::CW;
+    V xr[Cfg::XBT][RJ], xn[Cfg::XBT][RJ];
+    S cw[Cfg::XBT][RJ], cn[Cfg::XBT][RJ];
+    S clast = 0, cln = 0;
+    auto prefetch = [&](int h, V (&xv)[Cfg::XBT][RJ], S (&cv)[Cfg::XBT][RJ], S &cl) {
         const T *xh = xb + h * P;
         const S *cu = cumb + (int64_t)h * p.nc * Q;
 #pragma unroll
         for (int k = 0; k < Cfg::XBT; ++k) {
             const int blk = tid + k * THREADS;
             if (blk < Cfg::XB) {
-                const int jb = blk / (P / 4), pb = blk % (P / 4);
-                load_block<T, RJ>(xh, HP, jb * RJ, pb * 4, Qc, xr[k]);
+                const int jb = blk / (P / CW), pb = blk % (P / CW);
+                load_block<T, RJ>(xh, HP, jb * RJ, pb * CW, Qc, xv[k]);
+                // the block's RJ consecutive decay sums, as 16-byte loads
 #pragma unroll
-                for (int i = 0; i < RJ; ++i) cw[k][i] = cu[jb * RJ + i];
+                for (int q = 0; q < RJ * (int)sizeof(S) / 16; ++q) {
+                    const uint4 u = reinterpret_cast<const uint4 *>(cu + jb * RJ)[q];
+                    __builtin_memcpy(reinterpret_cast<unsigned char *>(cv[k]) + 16 * q, &u, 16);
+                }
             }
         }
-        clast = cu[Q - 1];
+        cl = cu[Q - 1];
     };
-    prefetch(h0);
+    prefetch(h0, xr, cw, clast);
 
     // B chunk -> LDS, transposed: bt[n][j]
     {
         const T *Bb = reinterpret_cast<const T *>(p.B) + (int64_t)b * p.bc_bs + (int64_t)t0 * p.G * N + grp * N;
         for (int blk = tid; blk < Cfg::BB; blk += THREADS) {
-            const int jb = blk / (N / 4), nb = blk % (N / 4);
-            F r[RJ];
-            load_block<T, RJ>(Bb, (int64_t)p.G * N, jb * RJ, nb * 4, Qc, r);
-            store_block_t<T, RJ, RS, false>(bt, jb * RJ, nb * 4, r, nullptr);
+            const int jb = blk / (N / CW), nb = blk % (N / CW);
+            V r[RJ];
+            load_block<T, RJ>(Bb, (int64_t)p.G * N, jb * RJ, nb * CW, Qc, r);
+            store_block_t<T, RJ, RS, false>(bt, jb * RJ, nb * CW, r, nullptr);
         }
     }
     __syncthreads();
@@ -144,19 +166,22 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_k
     const int64_t PN = (int64_t)P * N;
     for (int h = h0, it = 0; h < h1; ++h, ++it) {
         T *xw = (it & 1) ? xw1 : xw0;
+        // the next head's loads are issued first, so they are in flight for this whole
+        // head (scaling, products and stores)
+        if (Cfg::EARLY && h + 1 < h1) prefetch(h + 1, xn, cn, cln);
         // scale by the decay to the chunk end, transpose into LDS
 #pragma unroll
         for (int k = 0; k < Cfg::XBT; ++k) {
             const int blk = tid + k * THREADS;
             if (blk < Cfg::XB) {
-                const int jb = blk / (P / 4), pb = blk % (P / 4);
+                const int jb = blk / (P / CW), pb = blk % (P / CW);
                 float w[RJ];
 #pragma unroll
-                for (int i = 0; i < RJ; ++i) w[i] = expf((float)(clast - cw[k][i]));
-                store_block_t<T, RJ, RS, true>(xw, jb * RJ, pb * 4, xr[k], w);
+                for (int i = 0; i < RJ; ++i) w[i] = __expf((float)(clast - cw[k][i]));
+                store_block_t<T, RJ, RS, true>(xw, jb * RJ, pb * CW, xr[k], w);
             }
         }
-        if (h + 1 < h1) prefetch(h + 1);
+        if (!Cfg::EARLY && h + 1 < h1) prefetch(h + 1, xr, cw, clast);
         __syncthreads();
 
         f32x4 acc[Cfg::NTW][Cfg::PT];
@@ -183,6 +208,16 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_k
 #pragma unroll
             for (int pt = 0; pt < Cfg::PT; ++pt)
                 *reinterpret_cast<F *>(out + ((nt * Cfg::PT + pt) * 64 + lane) * 4) = frag_from_f32<T>(acc[i][pt]);
+        }
+        if (Cfg::EARLY && h + 1 < h1) {
+#pragma unroll
+            for (int k = 0; k < Cfg::XBT; ++k)
+#pragma unroll
+                for (int i = 0; i < RJ; ++i) {
+                    xr[k][i] = xn[k][i];
+                    cw[k][i] = cn[k][i];
+                }
+            clast = cln;
         }
     }
 }
