@@ -44,11 +44,13 @@ __device__ __forceinline__ void store_run(V *dst, const V (&v)[E]) {
 }
 
 template <typename T, int Q>
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p) {
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
     typedef typename CumT<T>::type S;
     constexpr int E = Q / 64;                    // values per lane
     __shared__ S tile[kCumHeads][Q + 1];
-    const int c = blockIdx.x, hb = blockIdx.y * kCumHeads, b = blockIdx.z;
+    const int c = blockIdx.x, hb = blockIdx.y * kCumHeads, b = blockIdx.z % p0.batch;
+    const Problem p = step_problem(p0, blockIdx.z / p0.batch);
+    if (c >= p.nc) return;                       // past a short last segment (uniform)
     const int t0 = c * Q;
     const int Qc = min(Q, p.L - t0);
     const T *dt = reinterpret_cast<const T *>(p.dt) + (int64_t)b * p.dt_bs;
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p) {
 }
 
 hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s) {
-    dim3 grid(p.nc, (p.H + kCumHeads - 1) / kCumHeads, p.batch);
+    dim3 grid(p.nc, (p.H + kCumHeads - 1) / kCumHeads, p.batch * step_count(p));
     if (p.dtype == 1) {
         if (p.Q == 64) chunk_cumsum_kernel<bf16, 64><<<grid, 256, 0, s>>>(p);
         else if (p.Q == 128) chunk_cumsum_kernel<bf16, 128><<<grid, 256, 0, s>>>(p);

@@ -279,7 +279,8 @@ template <int YPIECES>
 __device__ __forceinline__ int ysw(int r) { return r & ((YPIECES < 8 ? YPIECES : 8) - 1); }
 
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_kernel(Problem p) {
+__global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_kernel(Problem p0) {
+    const Problem p = step_problem(p0, blockIdx.y);
     using Cfg = ScanCfg<T, Q, P, N>;
     using Buf = HeadBuf<T, Q, P, N>;
     using F = typename TF<T>::type;
@@ -308,7 +309,8 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int hgi = logical % nhg;
     const int bc = logical / nhg;
-    const int c = bc % p.nc, b = bc / p.nc;
+    const int c = bc % p0.nc, b = bc / p0.nc;     // grid layout: chunks of the longest step
+    if (c >= p.nc) return;                        // past a short last segment (uniform)
     const int grp = hgi / hg_per_group;
     const int h0 = grp * hpg + (hgi % hg_per_group) * p.heads_per_wg_scan;
     const int h1 = min(h0 + p.heads_per_wg_scan, (grp + 1) * hpg);
@@ -528,7 +530,7 @@ static hipError_t launch_scan_t(const Problem &p, hipStream_t s) {
         const int nhg = p.G * ((hpg + p.heads_per_wg_scan - 1) / p.heads_per_wg_scan);
         const int64_t nblk = (int64_t)p.batch * p.nc * nhg;
         if (nblk <= 0 || nblk > 0x7fffffff) return hipErrorInvalidValue;
-        chunk_scan_kernel<T, Q, P, N><<<(unsigned)nblk, Cfg::THREADS, Cfg::LDS, s>>>(p);
+        chunk_scan_kernel<T, Q, P, N><<<dim3((unsigned)nblk, step_count(p)), Cfg::THREADS, Cfg::LDS, s>>>(p);
         return hipGetLastError();
     }
 }

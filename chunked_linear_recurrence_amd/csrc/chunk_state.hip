@@ -87,7 +87,8 @@ __device__ __forceinline__ void store_block_t(T *lds, int j0, int c0, const type
 
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) __attribute__((amdgpu_waves_per_eu(StateCfg<T, Q, P, N>::WPE)))
-void chunk_state_kernel(Problem p) {
+void chunk_state_kernel(Problem p0) {
+    const Problem p = step_problem(p0, blockIdx.y);
     using Cfg = StateCfg<T, Q, P, N>;
     using F = typename TF<T>::type;
     typedef typename CumT<T>::type S;
@@ -104,7 +105,8 @@ void chunk_state_kernel(Problem p) {
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int hgi = logical % nhg;
     const int bc = logical / nhg;
-    const int c = bc % p.nc, b = bc / p.nc;
+    const int c = bc % p0.nc, b = bc / p0.nc;     // grid layout: chunks of the longest step
+    if (c >= p.nc) return;                        // past a short last segment (uniform)
     const int grp = hgi / hg_per_group;
     const int h0 = grp * hpg + (hgi % hg_per_group) * p.heads_per_wg_state;
     const int h1 = min(h0 + p.heads_per_wg_state, (grp + 1) * hpg);
@@ -235,7 +237,7 @@ static hipError_t launch_state_t(const Problem &p, hipStream_t s) {
         static const hipError_t attr = hipFuncSetAttribute(
             (const void *)chunk_state_kernel<T, Q, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
         if (attr != hipSuccess) return attr;
-        chunk_state_kernel<T, Q, P, N><<<(unsigned)nblk, Cfg::THREADS, Cfg::LDS, s>>>(p);
+        chunk_state_kernel<T, Q, P, N><<<dim3((unsigned)nblk, step_count(p)), Cfg::THREADS, Cfg::LDS, s>>>(p);
         return hipGetLastError();
     }
 }

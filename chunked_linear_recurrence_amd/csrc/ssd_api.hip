@@ -137,7 +137,7 @@ int heads_per_wg(int64_t units, int64_t hpg, int64_t target, const char *env) {
     return (int)hg;
 }
 
-ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q) {
+ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q, int steps = 1) {
     ssd::Problem p;
     memset(&p, 0, sizeof(p));
     p.batch = (int)d.batch;
@@ -149,7 +149,7 @@ ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q) {
     p.Q = Q;
     p.nc = (int)((L + Q - 1) / Q);
     p.dtype = d.dtype;
-    const int64_t units = d.batch * p.nc * d.ngroups;
+    const int64_t units = d.batch * p.nc * d.ngroups * steps;
     const int64_t hpg = d.nheads / d.ngroups;
     p.heads_per_wg_state = heads_per_wg(units, hpg, 1024, "SSD_HEADS_PER_WG_STATE");
     p.heads_per_wg_scan = heads_per_wg(units, hpg, 512, "SSD_HEADS_PER_WG_SCAN");
@@ -272,26 +272,40 @@ ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_
     return ok();
 }
 
-// Segmented (vertical) stack: workspace = two activation buffers of one segment + one
-// layer's workspace over one segment.
-static bool seg_layout(const ssd_dims_t &d, int32_t Q, int64_t V, size_t *act_off, size_t *act_bytes_each,
-                       size_t *layer_off, size_t *total) {
-    const int64_t Vs = V < d.seqlen ? V : d.seqlen;
-    Layout lo;
-    if (!layout_for(d, Vs, Q, &lo)) return false;
-    const size_t a = align_up((size_t)(d.batch * Vs * d.nheads * d.headdim) * (size_t)act_bytes(d.dtype));
-    *act_off = 0;
-    *act_bytes_each = a;
-    *layer_off = 2 * a;
-    *total = 2 * a + lo.total;
+// Segmented (vertical) stack: workspace = 2 * depth segment activation buffers + depth
+// layer workspaces over one segment (depth 1 without SSD_FLAG_WAVEFRONT).
+struct SegLayout {
+    int64_t Vs;          // tokens of the longest segment
+    int nseg, depth;
+    size_t act_each, lws_each, act_off, lws_off, total;
+    Layout lo;           // one layer workspace over Vs tokens
+};
+
+static bool seg_layout(const ssd_dims_t &d, int32_t Q, int64_t V, int32_t n_layers, uint32_t flags,
+                       SegLayout *sl) {
+    if (V < 1 || n_layers < 1) return false;
+    sl->Vs = V < d.seqlen ? V : d.seqlen;
+    const int64_t nseg = (d.seqlen + V - 1) / V;
+    if (nseg > INT32_MAX) return false;
+    sl->nseg = (int)nseg;
+    sl->depth = (flags & SSD_FLAG_WAVEFRONT) ? (int)(nseg < n_layers ? nseg : n_layers) : 1;
+    if (!layout_for(d, sl->Vs, Q, &sl->lo)) return false;
+    int64_t act;
+    if (!mul_ok(d.batch * sl->Vs, d.nheads * d.headdim, INT64_C(1) << 60, &act)) return false;
+    sl->act_each = align_up((size_t)act * (size_t)act_bytes(d.dtype));
+    sl->lws_each = sl->lo.total;
+    sl->act_off = 0;
+    sl->lws_off = 2 * (size_t)sl->depth * sl->act_each;
+    sl->total = sl->lws_off + (size_t)sl->depth * sl->lws_each;
     return true;
 }
 
-size_t ssd_segmented_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q, int64_t V) {
-    if (check_dims(dims, chunk_Q) != SSD_OK || V < 1) return 0;
-    size_t a, ae, l, t;
-    if (!seg_layout(*dims, chunk_Q, V, &a, &ae, &l, &t)) return 0;
-    return t;
+size_t ssd_segmented_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q, int64_t V, int32_t n_layers,
+                                     uint32_t flags) {
+    if (check_dims(dims, chunk_Q) != SSD_OK || (flags & ~(SSD_FLAG_RESIDUAL | SSD_FLAG_WAVEFRONT))) return 0;
+    SegLayout sl;
+    if (!seg_layout(*dims, chunk_Q, V, n_layers, flags, &sl)) return 0;
+    return sl.total;
 }
 
 ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, int64_t V, const void *x0,
@@ -305,68 +319,106 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
     if (V < 1) return fail(SSD_ERR_BAD_SHAPE, "V must be >= 1 (got %lld)", (long long)V);
     if (!x0 || !dt || !A || !B || !C || !layer_states || !y)
         return fail(SSD_ERR_NULL_ARG, "x0, dt, A, B, C, layer_states and y must be non-NULL");
-    if (flags & ~SSD_FLAG_RESIDUAL) return fail(SSD_ERR_BAD_SHAPE, "unknown flag bits 0x%x", flags);
+    if (flags & ~(SSD_FLAG_RESIDUAL | SSD_FLAG_WAVEFRONT))
+        return fail(SSD_ERR_BAD_SHAPE, "unknown flag bits 0x%x", flags);
     if (st = check_alignment(x0, dt, A, B, C, D, layer_states, y, layer_states, workspace, d.dtype); st != SSD_OK)
         return st;
-    size_t act_off, act_each, layer_off, total;
-    if (!seg_layout(d, chunk_Q, V, &act_off, &act_each, &layer_off, &total))
-        return fail(SSD_ERR_BAD_SHAPE, "sizes overflow");
-    if (!workspace || workspace_bytes < total)
+    SegLayout sl;
+    if (!seg_layout(d, chunk_Q, V, n_layers, flags, &sl)) return fail(SSD_ERR_BAD_SHAPE, "sizes overflow");
+    if (!workspace || workspace_bytes < sl.total)
         return fail(SSD_ERR_WORKSPACE, "workspace %p of %zu bytes; %zu bytes are needed", workspace,
-                    workspace_bytes, total);
+                    workspace_bytes, sl.total);
     const size_t e = (size_t)act_bytes(d.dtype);
     const size_t nx = (size_t)(d.batch * d.seqlen * d.nheads * d.headdim) * e;
     const size_t ns = (size_t)n_layers * (size_t)(d.batch * d.nheads * d.headdim * d.dstate) * 4;
     if (overlap(y, nx, x0, nx)) return fail(SSD_ERR_ALIAS, "y overlaps x0");
-    if (overlap(workspace, total, x0, nx) || overlap(workspace, total, y, nx) ||
-        overlap(workspace, total, layer_states, ns) || overlap(layer_states, ns, y, nx))
+    if (overlap(workspace, sl.total, x0, nx) || overlap(workspace, sl.total, y, nx) ||
+        overlap(workspace, sl.total, layer_states, ns) || overlap(layer_states, ns, y, nx))
         return fail(SSD_ERR_ALIAS, "workspace, layer_states and y must not overlap each other or x0");
 
     unsigned char *ws = static_cast<unsigned char *>(workspace);
-    void *act[2] = {ws + act_off, ws + act_off + act_each};
-    const int64_t Vs = V < d.seqlen ? V : d.seqlen;
-    Layout lo;
-    layout_for(d, Vs, chunk_Q, &lo);
-    unsigned char *lws = ws + layer_off;
-    const int64_t HP = d.nheads * d.headdim, GN = d.ngroups * d.dstate;
-    const int64_t state_elems = d.batch * d.nheads * d.headdim * d.dstate;
     hipStream_t s = static_cast<hipStream_t>(stream);
-
-    for (int64_t s0 = 0; s0 < d.seqlen; s0 += V) {
-        const int64_t len = (d.seqlen - s0) < V ? (d.seqlen - s0) : V;
-        for (int l = 0; l < n_layers; ++l) {
-            ssd::Problem p = make_problem(d, len, chunk_Q);
-            if (l == 0) {
-                p.x = static_cast<const unsigned char *>(x0) + (size_t)(s0 * HP) * e;
-                p.x_bs = d.seqlen * HP;
-            } else {
-                p.x = act[(l - 1) & 1];
-                p.x_bs = Vs * HP;
+    // Every step (segment s, layer l) is the same layer call in both schedules; only how
+    // many of them share a launch differs.  The steps of anti-diagonal dg are segments
+    // s_lo..s_hi with l = dg - s.
+    const int S = sl.nseg;
+    const int last_diag = S - 1 + n_layers - 1;
+    for (int dg = 0; sl.depth > 1 && dg <= last_diag; ++dg) {
+        const int s_lo = dg - (n_layers - 1) > 0 ? dg - (n_layers - 1) : 0;
+        const int s_hi = dg < S - 1 ? dg : S - 1;
+        ssd::Problem p = make_problem(d, sl.Vs, chunk_Q, s_hi - s_lo + 1);
+        p.flags = flags & SSD_FLAG_RESIDUAL;
+        ssd::Steps &q = p.st;
+        q.count = s_hi - s_lo + 1;
+        q.d = dg;
+        q.s_first = s_lo;
+        q.n_layers = n_layers;
+        q.depth = sl.depth;
+        q.V = V;
+        q.Ltotal = d.seqlen;
+        q.x0 = x0;
+        q.y_out = y;
+        q.act = ws + sl.act_off;
+        q.act_each = sl.act_each;
+        q.lws = ws + sl.lws_off;
+        q.lws_each = sl.lws_each;
+        q.o_dA = sl.lo.dA;
+        q.o_bintra = sl.lo.bintra;
+        q.o_bin = sl.lo.bin;
+        q.o_decF = sl.lo.decF;
+        q.o_decG = sl.lo.decG;
+        q.dt0 = dt;
+        q.B0 = B;
+        q.C0 = C;
+        q.A0 = A;
+        q.D0 = D;
+        q.states = layer_states;
+        st = run_layer(p, s, 1, kStages);
+        if (st != SSD_OK) return st;
+    }
+    if (sl.depth == 1) {
+        // one step at a time, in the page's order: segment s through every layer, then
+        // segment s + 1
+        void *act[2] = {ws + sl.act_off, ws + sl.act_off + sl.act_each};
+        unsigned char *lws = ws + sl.lws_off;
+        const int64_t HP = d.nheads * d.headdim, GN = d.ngroups * d.dstate;
+        const int64_t state_elems = d.batch * d.nheads * d.headdim * d.dstate;
+        for (int64_t s0 = 0; s0 < d.seqlen; s0 += V) {
+            const int64_t len = (d.seqlen - s0) < V ? (d.seqlen - s0) : V;
+            for (int l = 0; l < n_layers; ++l) {
+                ssd::Problem p = make_problem(d, len, chunk_Q);
+                if (l == 0) {
+                    p.x = static_cast<const unsigned char *>(x0) + (size_t)(s0 * HP) * e;
+                    p.x_bs = d.seqlen * HP;
+                } else {
+                    p.x = act[(l - 1) & 1];
+                    p.x_bs = sl.Vs * HP;
+                }
+                if (l == n_layers - 1) {
+                    p.y = static_cast<unsigned char *>(y) + (size_t)(s0 * HP) * e;
+                    p.y_bs = d.seqlen * HP;
+                } else {
+                    p.y = act[l & 1];
+                    p.y_bs = sl.Vs * HP;
+                }
+                p.dt = static_cast<const unsigned char *>(dt) + (size_t)(s0 * d.nheads) * e;
+                p.dt_bs = d.seqlen * d.nheads;
+                p.B = static_cast<const unsigned char *>(B) + (size_t)(s0 * GN) * e;
+                p.C = static_cast<const unsigned char *>(C) + (size_t)(s0 * GN) * e;
+                p.bc_bs = d.seqlen * GN;
+                p.A = A + (size_t)l * d.nheads;
+                p.D = D ? D + (size_t)l * d.nheads : nullptr;
+                p.init = layer_states + (size_t)l * state_elems;
+                p.final_state = layer_states + (size_t)l * state_elems;
+                p.flags = flags & SSD_FLAG_RESIDUAL;
+                p.dA_cum = lws + sl.lo.dA;
+                p.b_intra = lws + sl.lo.bintra;
+                p.b_in = lws + sl.lo.bin;
+                p.decF = reinterpret_cast<float *>(lws + sl.lo.decF);
+                p.decG = reinterpret_cast<float *>(lws + sl.lo.decG);
+                st = run_layer(p, s, 1, kStages);
+                if (st != SSD_OK) return st;
             }
-            if (l == n_layers - 1) {
-                p.y = static_cast<unsigned char *>(y) + (size_t)(s0 * HP) * e;
-                p.y_bs = d.seqlen * HP;
-            } else {
-                p.y = act[l & 1];
-                p.y_bs = Vs * HP;
-            }
-            p.dt = static_cast<const unsigned char *>(dt) + (size_t)(s0 * d.nheads) * e;
-            p.dt_bs = d.seqlen * d.nheads;
-            p.B = static_cast<const unsigned char *>(B) + (size_t)(s0 * GN) * e;
-            p.C = static_cast<const unsigned char *>(C) + (size_t)(s0 * GN) * e;
-            p.bc_bs = d.seqlen * GN;
-            p.A = A + (size_t)l * d.nheads;
-            p.D = D ? D + (size_t)l * d.nheads : nullptr;
-            p.init = layer_states + (size_t)l * state_elems;
-            p.final_state = layer_states + (size_t)l * state_elems;
-            p.flags = flags;
-            p.dA_cum = lws + lo.dA;
-            p.b_intra = lws + lo.bintra;
-            p.b_in = lws + lo.bin;
-            p.decF = reinterpret_cast<float *>(lws + lo.decF);
-            p.decG = reinterpret_cast<float *>(lws + lo.decG);
-            st = run_layer(p, s, 1, kStages);
-            if (st != SSD_OK) return st;
         }
     }
     return ok();

@@ -31,8 +31,31 @@ typedef __bf16 bf16;
 
 constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 
+// A batch of steps (segment s, layer l) of the vertical stack that run in one launch:
+// step k of the batch is segment s = s_first + k of layer l = d - s (all steps of one
+// anti-diagonal d = s + l are independent).  Every step is one layer call over one
+// segment; its pointers follow from the stack's buffers (see step_problem below).
+struct Steps {
+    int count;                 // steps in this launch; 0: not a stack launch
+    int d, s_first, n_layers, depth;
+    int64_t V, Ltotal;         // segment length, tokens of the whole sequence
+    const void *x0;            // stack input [batch, Ltotal, H, P]
+    void *y_out;               // stack output, same layout
+    unsigned char *act;        // [2][depth] segment activation buffers of act_each bytes
+    size_t act_each;
+    unsigned char *lws;        // [depth] layer workspaces of lws_each bytes
+    size_t lws_each;
+    size_t o_dA, o_bintra, o_bin, o_decF, o_decG;   // offsets inside one layer workspace
+    const void *dt0, *B0, *C0; // full-sequence dt, B, C
+    const float *A0, *D0;      // [n_layers, H]; D0 may be null
+    float *states;             // [n_layers, batch, H, P, N]
+};
+
 // One layer's arguments, as the kernels see them.  Token t of batch row b of x/y is at
 // x + b * x_bs + t * H * P; dt at dt + b * dt_bs + t * H; B/C at B + b * bc_bs + t * G * N.
+// For a stack launch (st.count > 0) the fields describe the longest step of the batch
+// (L = V, nc = chunks of V): they size the grid, and each block takes its own step's
+// fields from step_problem().
 struct Problem {
     int batch, L, H, P, N, G, Q, nc;
     int dtype;                 // 0 = f32, 1 = bf16
@@ -51,7 +74,63 @@ struct Problem {
     void *b_in;        // [batch, nc, H, P*N] tile order, act dtype
     int heads_per_wg_state;   // head group of chunk_state
     int heads_per_wg_scan;    // head group of chunk_scan
+    Steps st;
 };
+
+// Steps in one launch (1 for a plain layer call).
+__host__ __device__ inline int step_count(const Problem &p) { return p.st.count > 0 ? p.st.count : 1; }
+
+// The arguments of step k of a stack launch (p itself for a plain layer call).  Segment s
+// covers tokens [s V, s V + len); layer 0 reads the stack input, the last layer writes the
+// stack output, and layer l in between reads the buffer layer l-1 wrote for the same
+// segment: act[(l-1) & 1][s % depth] (the steps of one diagonal have distinct s % depth,
+// and a buffer is rewritten only after its reader, one diagonal later, has run).  Layer
+// l's state (init and final) is states[l]; the step's intermediates use workspace slot
+// s % depth.
+__device__ __forceinline__ Problem step_problem(const Problem &p, int k) {
+    if (p.st.count == 0) return p;
+    const Steps &st = p.st;
+    Problem q = p;
+    const int s = st.s_first + k, l = st.d - s;
+    const int64_t s0 = (int64_t)s * st.V;
+    const int64_t len = min(st.V, st.Ltotal - s0);
+    q.L = (int)len;
+    q.nc = (int)((len + p.Q - 1) / p.Q);
+    const int64_t e = p.dtype == 1 ? 2 : 4;
+    const int64_t HP = (int64_t)p.H * p.P, GN = (int64_t)p.G * p.N;
+    const int slot = s % st.depth;
+    if (l == 0) {
+        q.x = static_cast<const unsigned char *>(st.x0) + s0 * HP * e;
+        q.x_bs = st.Ltotal * HP;
+    } else {
+        q.x = st.act + (size_t)(((l - 1) & 1) * st.depth + slot) * st.act_each;
+        q.x_bs = st.V * HP;
+    }
+    if (l == st.n_layers - 1) {
+        q.y = static_cast<unsigned char *>(st.y_out) + s0 * HP * e;
+        q.y_bs = st.Ltotal * HP;
+    } else {
+        q.y = st.act + (size_t)((l & 1) * st.depth + slot) * st.act_each;
+        q.y_bs = st.V * HP;
+    }
+    q.dt = static_cast<const unsigned char *>(st.dt0) + s0 * p.H * e;
+    q.dt_bs = st.Ltotal * p.H;
+    q.B = static_cast<const unsigned char *>(st.B0) + s0 * GN * e;
+    q.C = static_cast<const unsigned char *>(st.C0) + s0 * GN * e;
+    q.bc_bs = st.Ltotal * GN;
+    q.A = st.A0 + (size_t)l * p.H;
+    q.D = st.D0 ? st.D0 + (size_t)l * p.H : nullptr;
+    float *ls = st.states + (size_t)l * p.batch * HP * p.N;
+    q.init = ls;
+    q.final_state = ls;
+    unsigned char *w = st.lws + (size_t)slot * st.lws_each;
+    q.dA_cum = w + st.o_dA;
+    q.b_intra = w + st.o_bintra;
+    q.b_in = w + st.o_bin;
+    q.decF = reinterpret_cast<float *>(w + st.o_decF);
+    q.decG = reinterpret_cast<float *>(w + st.o_decG);
+    return q;
+}
 
 hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_state(const Problem &p, hipStream_t s);

@@ -45,13 +45,14 @@ __device__ __forceinline__ float4 fma4(float a, const float4 &s, const float4 &b
 }
 
 template <typename T>
-__global__ __launch_bounds__(64) void state_pass_kernel(Problem p) {
+__global__ __launch_bounds__(64) void state_pass_kernel(Problem p0) {
+    const Problem p = step_problem(p0, blockIdx.z / p0.batch);
     typedef typename TF<T>::type V;
     typedef typename CumT<T>::type S;
     constexpr int K = sizeof(T) == 2 ? 16 : 8;         // chunks per load group
     const int PN = p.P * p.N;
     const int e4 = blockIdx.x * 64 + threadIdx.x;        // 4-element group within one state
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.y, b = blockIdx.z % p0.batch;
     if (e4 * 4 >= PN) return;
     const int e = e4 * 4;
     const int tile = e >> 8, l = (e >> 2) & 63;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(64) void state_pass_kernel(Problem p) {
 
 hipError_t launch_state_pass(const Problem &p, hipStream_t s) {
     const int PN = p.P * p.N;
-    dim3 grid((PN / 4 + 63) / 64, p.H, p.batch);
+    dim3 grid((PN / 4 + 63) / 64, p.H, p.batch * step_count(p));
     if (p.dtype == 1) state_pass_kernel<bf16><<<grid, 64, 0, s>>>(p);
     else state_pass_kernel<float><<<grid, 64, 0, s>>>(p);
     return hipGetLastError();

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "_build", "libssdscan.so")
 
 SSD_F32, SSD_BF16 = 0, 1
 SSD_FLAG_RESIDUAL = 1
+SSD_FLAG_WAVEFRONT = 2
 
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_BAD_DTYPE",
           4: "SSD_ERR_UNSUPPORTED", 5: "SSD_ERR_MISALIGNED", 6: "SSD_ERR_WORKSPACE",
@@ -56,7 +57,7 @@ def lib():
         L.ssd_chunk_scan_fwd.restype = ctypes.c_int
         L.ssd_chunk_scan_stages.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp, i32, i32]
         L.ssd_chunk_scan_stages.restype = ctypes.c_int
-        L.ssd_segmented_workspace_bytes.argtypes = [dp, i32, i64]
+        L.ssd_segmented_workspace_bytes.argtypes = [dp, i32, i64, i32, u32]
         L.ssd_segmented_workspace_bytes.restype = sz
         L.ssd_chunk_scan_segmented.argtypes = [dp, i32, i64, vp, vp, vp, vp, vp, vp, vp, i32, u32, vp, vp, sz, vp]
         L.ssd_chunk_scan_segmented.restype = ctypes.c_int
@@ -105,8 +106,9 @@ def workspace_bytes(dims, chunk) -> int:
     return lib().ssd_chunk_scan_workspace_bytes(ctypes.byref(dims), chunk)
 
 
-def segmented_workspace_bytes(dims, chunk, V) -> int:
-    return lib().ssd_segmented_workspace_bytes(ctypes.byref(dims), chunk, V)
+def segmented_workspace_bytes(dims, chunk, V, n_layers=1, wavefront=False) -> int:
+    flags = SSD_FLAG_WAVEFRONT if wavefront else 0
+    return lib().ssd_segmented_workspace_bytes(ctypes.byref(dims), chunk, V, n_layers, flags)
 
 
 NSTAGES = 4   # chunk_cumsum, chunk_state, state_pass, chunk_scan
@@ -148,16 +150,17 @@ def fwd(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y=None, final_sta
 
 
 def segmented(x0, dt, A, B, C, D, layer_states, V, chunk=256, *, y=None, residual=True,
-              workspace=None, stream=None):
-    """Vertical layer stack (ssd_chunk_scan_segmented); layer_states is updated in place."""
+              wavefront=True, workspace=None, stream=None):
+    """Vertical layer stack (ssd_chunk_scan_segmented); layer_states is updated in place.
+    wavefront=False runs the (segment, layer) steps strictly one at a time."""
     dims = dims_of(x0, B)
     n_layers = A.shape[0]
-    nbytes = segmented_workspace_bytes(dims, chunk, V)
+    nbytes = segmented_workspace_bytes(dims, chunk, V, n_layers, wavefront)
     if workspace is None:
         workspace = alloc_workspace(nbytes, x0.device)
     if y is None:
         y = torch.empty_like(x0)
-    flags = SSD_FLAG_RESIDUAL if residual else 0
+    flags = (SSD_FLAG_RESIDUAL if residual else 0) | (SSD_FLAG_WAVEFRONT if wavefront else 0)
     _check(lib().ssd_chunk_scan_segmented(ctypes.byref(dims), n_layers, V, _ptr(x0), _ptr(dt), _ptr(A),
                                           _ptr(B), _ptr(C), _ptr(D), _ptr(layer_states), chunk, flags,
                                           _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))

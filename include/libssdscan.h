@@ -95,6 +95,8 @@ typedef struct ssd_dims {
 
 /* flags */
 #define SSD_FLAG_RESIDUAL 1u   /* y = (recurrence output + D x) + x, rounded once to act */
+#define SSD_FLAG_WAVEFRONT 2u  /* segmented stack only: run independent (segment, layer)
+                                  steps together (see ssd_chunk_scan_segmented) */
 
 /* Size in bytes of the workspace ssd_chunk_scan_fwd needs for these dims and chunk_Q,
  * or 0 when the arguments are invalid.  The workspace holds the per-chunk log-decay
@@ -117,10 +119,14 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, const void *x, const voi
                                 void *y, float *final_state, uint32_t flags,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace size for ssd_chunk_scan_segmented (0 when the arguments are invalid).  It
- * depends on V, not on seqlen: memory stays at one segment plus the caller's per-layer
- * states, whatever the sequence length [分块推理 §3.2]. */
-size_t ssd_segmented_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q, int64_t V);
+/* Workspace size for ssd_chunk_scan_segmented with these n_layers and flags (0 when the
+ * arguments are invalid).  Without SSD_FLAG_WAVEFRONT it is two segment buffers and one
+ * layer workspace over V tokens; with it, depth = min(ceil(seqlen / V), n_layers) times
+ * that.  Either way it is bounded independently of seqlen: memory stays at a fixed number
+ * of segments plus the caller's per-layer states, whatever the sequence length
+ * [分块推理 §3.2]. */
+size_t ssd_segmented_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q, int64_t V,
+                                     int32_t n_layers, uint32_t flags);
 
 /* A stack of n_layers layers run in the vertical order of [分块推理 §3.2]: the sequence is
  * cut into segments of V tokens (the last may be shorter); each segment goes through
@@ -136,10 +142,18 @@ size_t ssd_segmented_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q, in
  *                      between calls resumes the stack exactly.
  *   y                  stack output [batch, L, nheads, headdim] (act): the last layer's
  *                      output; must not overlap x0.
- *   flags              0 or SSD_FLAG_RESIDUAL (applied at every layer).
+ *   flags              SSD_FLAG_RESIDUAL (applied at every layer) and/or
+ *                      SSD_FLAG_WAVEFRONT.
  * Layer l maps u to (recurrence_l(u) + D_l u [+ u]) rounded to act.  When V is a multiple
  * of chunk_Q the result is bit-identical to running ssd_chunk_scan_fwd layer by layer over
- * the whole sequence (the horizontal order of [分块推理 §3.1]). */
+ * the whole sequence (the horizontal order of [分块推理 §3.1]).
+ * Schedule: step (s, l) is segment s through layer l.  It needs (s, l-1) (its input) and
+ * (s-1, l) (layer l's state), nothing else.  Without SSD_FLAG_WAVEFRONT the steps run one
+ * at a time, segment by segment, as the page describes.  With it, all steps of one
+ * anti-diagonal s + l = const run in the same four kernel launches (up to
+ * min(segments, n_layers) steps at once), which fills the GPU when a single step is
+ * small; every step computes exactly what it computes alone, so the output and states
+ * are bit-identical between the two schedules. */
 ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, int64_t V,
                                       const void *x0, const void *dt, const float *A,
                                       const void *B, const void *C, const float *D,

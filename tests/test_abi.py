@@ -91,6 +91,13 @@ def test_segmented_argument_errors():
     assert seg(states=None) == 1
     assert seg(wsb=10) == 6
     assert seg(Q=96) == 4
+    d2 = _dims(L=512)
+    assert L.ssd_chunk_scan_segmented(ctypes.byref(d2), 2, 128, v(FAKE), v(FAKE + 2 ** 30), v(FAKE + 2 ** 31),
+                                      v(FAKE + 2 ** 32), v(FAKE + 2 ** 33), None, v(FAKE + 2 ** 36), 64, 4,
+                                      v(FAKE + 2 ** 34), v(FAKE + 2 ** 35), 1 << 30, None) == 2   # unknown flag
+    assert ssd.segmented_workspace_bytes(d2, 64, 128, 2, False) > 0
+    assert L.ssd_segmented_workspace_bytes(ctypes.byref(d2), 64, 128, 2, 4) == 0
+    assert L.ssd_segmented_workspace_bytes(ctypes.byref(d2), 64, 128, 0, 0) == 0
 
 
 def test_workspace_sizes_and_layout():
@@ -107,11 +114,17 @@ def test_workspace_sizes_and_layout():
         assert offs[2] - offs[1] >= states * e and offs[3] - offs[2] >= states * e
         assert all(o % 256 == 0 for o in offs) and nb >= offs[3]
         if w.segment:
-            segb = ssd.segmented_workspace_bytes(d, w.chunk, w.segment)
-            # memory depends on V, not on the sequence length
+            segb = ssd.segmented_workspace_bytes(d, w.chunk, w.segment, w.layers, False)
+            # memory depends on V (and, for the wavefront, on the layer count), not on the
+            # sequence length
             d2 = ssd.Dims(w.batch, 4 * w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d.dtype, 0)
-            assert ssd.segmented_workspace_bytes(d2, w.chunk, w.segment) == segb
+            d3 = ssd.Dims(w.batch, 8 * w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d.dtype, 0)
+            assert ssd.segmented_workspace_bytes(d2, w.chunk, w.segment, w.layers, False) == segb
             assert segb < nb
+            wf = [ssd.segmented_workspace_bytes(dd, w.chunk, w.segment, w.layers, True) for dd in (d, d2, d3)]
+            nseg = -(-w.seqlen // w.segment)
+            assert wf[0] == segb * min(nseg, w.layers)
+            assert wf[1] == wf[2] == segb * w.layers
     assert ssd.workspace_bytes(_dims(H=3, G=2), 64) == 0
 
 

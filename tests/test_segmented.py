@@ -19,12 +19,14 @@ def _stack(nl, b, L, H, P, N, dtype="bf16", seed=0):
     return inputs.make_stack(b, L, H, P, N, 1, nl, dtype, seed=seed)
 
 
-def test_small_stack_matches_oracle_and_horizontal():
+@pytest.mark.parametrize("wavefront", [False, True])
+def test_small_stack_matches_oracle_and_horizontal(wavefront):
     nl, b, L, H, P, N, Q, V = 4, 2, 1000, 3, 64, 64, 64, 256
     d = _stack(nl, b, L, H, P, N)
     g = to_dev(d, DEV)
     s_seg = torch.zeros(nl, b, H, P, N, device=DEV)
-    y_seg, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_seg, V, Q)
+    y_seg, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_seg, V, Q,
+                             wavefront=wavefront)
     s_hor = torch.zeros_like(s_seg)
     y_hor, _ = ssd.horizontal(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_hor, Q)
     torch.cuda.synchronize()
@@ -36,14 +38,15 @@ def test_small_stack_matches_oracle_and_horizontal():
         assert err_bf16(s_seg[l], fr[l]) <= 2e-2
 
 
-def test_fp32_stack_and_ragged_segments():
+@pytest.mark.parametrize("wavefront", [False, True])
+def test_fp32_stack_and_ragged_segments(wavefront):
     nl, b, L, H, P, N, Q = 3, 1, 700, 2, 16, 16, 64
     d = _stack(nl, b, L, H, P, N, dtype="f32", seed=1)
     g = to_dev(d, DEV)
     yr, fr = oracle.stack_horizontal(d["x0"], d["dt"], d["A"], d["B"], d["C"], d["D"], store_bf16=False)
     for V in (64, 128, 100, 700, 5000):            # 100 is not a multiple of Q
         s = torch.zeros(nl, b, H, P, N, device=DEV)
-        y, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s, V, Q)
+        y, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s, V, Q, wavefront=wavefront)
         torch.cuda.synchronize()
         assert err_f32(y, yr) <= 1e-4, V
         for l in range(nl):
@@ -72,6 +75,27 @@ def test_resume_from_host_copy_is_bit_identical():
     assert torch.equal(s2, s_full)
 
 
+@pytest.mark.parametrize("dtype,nl,L,V,Q,P,N", [
+    ("bf16", 5, 1000, 128, 64, 64, 64),    # more segments (8) than layers, ragged last segment
+    ("bf16", 6, 300, 128, 64, 32, 64),     # fewer segments (3) than layers
+    ("f32", 4, 520, 64, 64, 16, 32),       # one segment per chunk, ragged tail
+    ("bf16", 3, 777, 100, 64, 64, 128),    # V not a multiple of Q
+])
+def test_wavefront_equals_one_step_at_a_time(dtype, nl, L, V, Q, P, N):
+    """The wavefront schedule runs the same (segment, layer) steps as the page's order, only
+    several per launch: outputs and final states are bit-identical."""
+    b, H = 2, 3
+    d = _stack(nl, b, L, H, P, N, dtype=dtype, seed=7)
+    g = to_dev(d, DEV)
+    init = torch.randn(nl, b, H, P, N, device=DEV) * 0.1
+    s1, s2 = init.clone(), init.clone()
+    y1, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s1, V, Q, wavefront=False)
+    y2, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s2, V, Q, wavefront=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(s1, s2)
+
+
 def test_swapped_layer_states_change_the_output():
     nl, b, L, H, P, N, Q, V = 2, 1, 512, 2, 64, 64, 64, 128
     d = _stack(nl, b, L, H, P, N, seed=3)
@@ -93,11 +117,14 @@ def test_vertical_stack_workload():
     shp = (nl, w.batch, w.nheads, w.headdim, w.dstate)
     s_seg = torch.zeros(shp, device=DEV)
     y_seg, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_seg, w.segment, w.chunk)
+    s_one = torch.zeros(shp, device=DEV)
+    y_one, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_one, w.segment, w.chunk,
+                             wavefront=False)
     s_hor = torch.zeros(shp, device=DEV)
     y_hor, _ = ssd.horizontal(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s_hor, w.chunk)
     torch.cuda.synchronize()
-    assert torch.equal(y_seg, y_hor)
-    assert torch.equal(s_seg, s_hor)
+    assert torch.equal(y_seg, y_hor) and torch.equal(y_one, y_hor)
+    assert torch.equal(s_seg, s_hor) and torch.equal(s_one, s_hor)
     T = 2 * w.segment
     yr, _ = oracle.stack_horizontal(d["x0"][:, :T], d["dt"][:, :T], d["A"], d["B"][:, :T], d["C"][:, :T],
                                     d["D"])
