@@ -13,6 +13,8 @@ Besides the headline tokens/s the line carries:
                 runs on, inside full steps) against the 8 TB/s peak;
   kernels       the same figures for all four kernels, plus matrix-core rates;
   end_to_end    the method's bytes / step time against peak HBM bandwidth;
+  stack         the 24-layer vertical stack (segmented entry point, wavefront and one
+                step at a time, and the horizontal order), a secondary figure;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores on the same inputs.
 
 Algorithmic bytes count every input a kernel needs once and every output it must write
@@ -43,6 +45,8 @@ def parse():
                          "the first ~20 ms of load); 0 disables")
     ap.add_argument("--workload", default=None, help="workload name (default: the 128K-token layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the secondary timing of the 24-layer vertical stack")
     ap.add_argument("--kernel-steps", type=int, default=0, help="launches per kernel for per-kernel timing "
                     "(default: --steps)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -110,6 +114,48 @@ def measured_traffic(workload, kernel):
     if t.get("source_sha256") != kernel_sources_sha256() or kernel not in t.get("kernels", {}):
         return None
     return t["kernels"][kernel]["bytes"]
+
+
+def stack_timing(torch, dev, reps=5):
+    """The 24-layer vertical stack (32768 tokens, V = 2048): the segmented entry point in
+    the wavefront schedule and one step at a time, and the horizontal order (one
+    ssd_chunk_scan_fwd per layer) for reference; HIP events around `reps` whole stacks."""
+    from chunked_linear_recurrence_amd import inputs, ssd, WORKLOADS
+    w = WORKLOADS["vertical_stack_24x_L32768_V2048"]
+    d = inputs.make(w)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    stream = torch.cuda.current_stream()
+    dims = ssd.dims_of(g["x0"], g["B"])
+    y = torch.empty_like(g["x0"])
+    states = torch.zeros(w.layers, w.batch, w.nheads, w.headdim, w.dstate, device=dev)
+    ws = {wf: ssd.alloc_workspace(ssd.segmented_workspace_bytes(dims, w.chunk, w.segment, w.layers, wf), dev)
+          for wf in (True, False)}
+
+    def seg(wf):
+        states.zero_()
+        ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], states, w.segment, w.chunk, y=y,
+                      wavefront=wf, workspace=ws[wf], stream=stream)
+
+    def hor():
+        states.zero_()
+        ssd.horizontal(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], states, w.chunk, stream=stream)
+
+    out = {"workload": w.name, "layers": w.layers, "tokens": w.tokens, "V": w.segment}
+    for name, f in (("wavefront", lambda: seg(True)), ("one_at_a_time", lambda: seg(False)),
+                    ("horizontal", hor)):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out["ms_" + name] = round(ms, 3)
+        out["layer_tokens_per_s_" + name] = round(w.layers * w.tokens / (ms * 1e-3), 1)
+    return out
 
 
 def cpu_baseline(d, w):
@@ -235,6 +281,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+    if not args.no_stack:
+        print("[bench] vertical stack", file=sys.stderr, flush=True)
+        out["stack"] = stack_timing(torch, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, w)

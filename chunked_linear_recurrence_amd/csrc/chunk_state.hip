@@ -15,9 +15,8 @@
 // dtype, transposed into LDS (double-buffered), and read as B-operand fragments; the
 // result tiles are rounded once to the activation dtype and stored in tile order, 4
 // values per lane (coalesced 512 B or 1 KiB per wave).
-// The next head's x rows and decays are loaded into registers at the start of the
-// current head (after its x is consumed, where registers are short), so their HBM
-// latency overlaps the head's work.
+// The next head's x rows and decays are loaded into registers as soon as the current
+// head's x is in LDS, so their HBM latency overlaps the current head's products.
 #include "ssd_common.h"
 
 namespace ssd {
@@ -37,12 +36,6 @@ struct StateCfg {
     static constexpr int BT_BYTES = N * RS * (int)sizeof(T);
     static constexpr int XW_BYTES = P * RS * (int)sizeof(T);
     static constexpr int LDS = BT_BYTES > 2 * XW_BYTES ? BT_BYTES : 2 * XW_BYTES;
-    // registers of one head's prefetched x rows and decays; when small, the next head's
-    // loads are issued at the start of the current head into a second register set (and
-    // the kernel is held to two waves per SIMD), otherwise after its x is consumed
-    static constexpr int XREGS = XBT * RJ * (16 + (int)sizeof(typename CumT<T>::type)) / 4;
-    static constexpr bool EARLY = XREGS <= 48;
-    static constexpr int WPE = EARLY ? 2 : 1;
     static constexpr bool OK = (KT % 2 == 0) && LDS <= kLdsBytes && NT % NWS == 0;
 };
 
@@ -86,8 +79,7 @@ __device__ __forceinline__ void store_block_t(T *lds, int j0, int c0, const type
 }
 
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) __attribute__((amdgpu_waves_per_eu(StateCfg<T, Q, P, N>::WPE)))
-void chunk_state_kernel(Problem p0) {
+__global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_kernel(Problem p0) {
     const Problem p = step_problem(p0, blockIdx.y);
     using Cfg = StateCfg<T, Q, P, N>;
     using F = typename TF<T>::type;
@@ -120,9 +112,9 @@ void chunk_state_kernel(Problem p0) {
     // x rows and decays of one head, loaded into registers one head ahead of their use
     typedef typename Row16T<T>::type V;
     constexpr int CW = Cfg::CW;
-    V xr[Cfg::XBT][RJ], xn[Cfg::XBT][RJ];
-    S cw[Cfg::XBT][RJ], cn[Cfg::XBT][RJ];
-    S clast = 0, cln = 0;
+    V xr[Cfg::XBT][RJ];
+    S cw[Cfg::XBT][RJ];
+    S clast = 0;
     auto prefetch = [&](int h, V (&xv)[Cfg::XBT][RJ], S (&cv)[Cfg::XBT][RJ], S &cl) {
         const T *xh = xb + h * P;
         const S *cu = cumb + (int64_t)h * p.nc * Q;
@@ -133,10 +125,22 @@ void chunk_state_kernel(Problem p0) {
                 const int jb = blk / (P / CW), pb = blk % (P / CW);
                 load_block<T, RJ>(xh, HP, jb * RJ, pb * CW, Qc, xv[k]);
                 // the block's RJ consecutive decay sums, as 16-byte loads
+                if constexpr (sizeof(S) == 4) {
 #pragma unroll
-                for (int q = 0; q < RJ * (int)sizeof(S) / 16; ++q) {
-                    const uint4 u = reinterpret_cast<const uint4 *>(cu + jb * RJ)[q];
-                    __builtin_memcpy(reinterpret_cast<unsigned char *>(cv[k]) + 16 * q, &u, 16);
+                    for (int q = 0; q < RJ / 4; ++q) {
+                        const float4 u = reinterpret_cast<const float4 *>(cu + jb * RJ)[q];
+                        cv[k][4 * q + 0] = u.x;
+                        cv[k][4 * q + 1] = u.y;
+                        cv[k][4 * q + 2] = u.z;
+                        cv[k][4 * q + 3] = u.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < RJ / 2; ++q) {
+                        const double2 u = reinterpret_cast<const double2 *>(cu + jb * RJ)[q];
+                        cv[k][2 * q + 0] = u.x;
+                        cv[k][2 * q + 1] = u.y;
+                    }
                 }
             }
         }
@@ -168,9 +172,6 @@ void chunk_state_kernel(Problem p0) {
     const int64_t PN = (int64_t)P * N;
     for (int h = h0, it = 0; h < h1; ++h, ++it) {
         T *xw = (it & 1) ? xw1 : xw0;
-        // the next head's loads are issued first, so they are in flight for this whole
-        // head (scaling, products and stores)
-        if (Cfg::EARLY && h + 1 < h1) prefetch(h + 1, xn, cn, cln);
         // scale by the decay to the chunk end, transpose into LDS
 #pragma unroll
         for (int k = 0; k < Cfg::XBT; ++k) {
@@ -183,7 +184,7 @@ void chunk_state_kernel(Problem p0) {
                 store_block_t<T, RJ, RS, true>(xw, jb * RJ, pb * CW, xr[k], w);
             }
         }
-        if (!Cfg::EARLY && h + 1 < h1) prefetch(h + 1, xr, cw, clast);
+        if (h + 1 < h1) prefetch(h + 1, xr, cw, clast);   // overlaps this head's products
         __syncthreads();
 
         f32x4 acc[Cfg::NTW][Cfg::PT];
@@ -210,16 +211,6 @@ void chunk_state_kernel(Problem p0) {
 #pragma unroll
             for (int pt = 0; pt < Cfg::PT; ++pt)
                 *reinterpret_cast<F *>(out + ((nt * Cfg::PT + pt) * 64 + lane) * 4) = frag_from_f32<T>(acc[i][pt]);
-        }
-        if (Cfg::EARLY && h + 1 < h1) {
-#pragma unroll
-            for (int k = 0; k < Cfg::XBT; ++k)
-#pragma unroll
-                for (int i = 0; i < RJ; ++i) {
-                    xr[k][i] = xn[k][i];
-                    cw[k][i] = cn[k][i];
-                }
-            clast = cln;
         }
     }
 }
