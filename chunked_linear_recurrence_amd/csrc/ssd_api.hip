@@ -424,6 +424,58 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
     return ok();
 }
 
+ssd_status_t ssd_step(const ssd_dims_t *dims, const void *x, const void *dt, const float *A, const void *B,
+                      const void *C, const float *D, float *state, void *y, uint32_t flags, void *stream) {
+    if (!dims) return fail(SSD_ERR_NULL_ARG, "dims is NULL");
+    const ssd_dims_t &d = *dims;
+    if (d.dtype != SSD_F32 && d.dtype != SSD_BF16)
+        return fail(SSD_ERR_BAD_DTYPE, "dtype %d is not SSD_F32 (0) or SSD_BF16 (1)", d.dtype);
+    if (d.reserved != 0) return fail(SSD_ERR_BAD_SHAPE, "dims.reserved must be 0");
+    if (d.seqlen != 1) return fail(SSD_ERR_BAD_SHAPE, "ssd_step takes one token: seqlen must be 1 (got %lld)",
+                                   (long long)d.seqlen);
+    if (d.batch <= 0 || d.nheads <= 0 || d.headdim <= 0 || d.dstate <= 0 || d.ngroups <= 0)
+        return fail(SSD_ERR_BAD_SHAPE, "every dimension must be >= 1");
+    if (d.nheads % d.ngroups != 0)
+        return fail(SSD_ERR_BAD_SHAPE, "nheads %lld is not a multiple of ngroups %lld", (long long)d.nheads,
+                    (long long)d.ngroups);
+    if (!ssd::step_supported((int)d.dstate))
+        return fail(SSD_ERR_UNSUPPORTED, "ssd_step supports dstate 16, 32, 64, 128 or 256 (got %lld)",
+                    (long long)d.dstate);
+    if (d.batch > 65535 || d.nheads > 65535 || d.headdim > (1 << 20))
+        return fail(SSD_ERR_UNSUPPORTED, "dimensions exceed the grid range");
+    if (!x || !dt || !A || !B || !C || !state || !y)
+        return fail(SSD_ERR_NULL_ARG, "x, dt, A, B, C, state and y must be non-NULL");
+    if (flags & ~SSD_FLAG_RESIDUAL) return fail(SSD_ERR_BAD_SHAPE, "unknown flag bits 0x%x", flags);
+    const uintptr_t e = (uintptr_t)act_bytes(d.dtype);
+    if (!aligned16(state) || !aligned16(B) || !aligned16(C))
+        return fail(SSD_ERR_MISALIGNED, "state, B and C must be 16-byte aligned");
+    if (((uintptr_t)x & (e - 1)) || ((uintptr_t)dt & (e - 1)) || ((uintptr_t)y & (e - 1)) ||
+        ((uintptr_t)A & 3u) || (D && ((uintptr_t)D & 3u)))
+        return fail(SSD_ERR_MISALIGNED, "x, dt, y, A or D is not aligned to its element size");
+    const size_t nx = (size_t)(d.batch * d.nheads * d.headdim) * e;
+    const size_t ns = (size_t)(d.batch * d.nheads * d.headdim * d.dstate) * 4;
+    if (overlap(y, nx, x, nx) || overlap(y, nx, state, ns)) return fail(SSD_ERR_ALIAS, "y overlaps x or state");
+    ssd::StepArgs a;
+    a.batch = (int)d.batch;
+    a.H = (int)d.nheads;
+    a.P = (int)d.headdim;
+    a.N = (int)d.dstate;
+    a.G = (int)d.ngroups;
+    a.dtype = d.dtype;
+    a.x = x;
+    a.dt = dt;
+    a.B = B;
+    a.C = C;
+    a.A = A;
+    a.D = D;
+    a.state = state;
+    a.y = y;
+    a.flags = flags;
+    const hipError_t err = ssd::launch_ssd_step(a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(SSD_ERR_HIP, "ssd_step launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
 const char *ssd_status_string(ssd_status_t status) {
     switch (status) {
         case SSD_OK: return "SSD_OK";

@@ -132,6 +132,22 @@ __device__ __forceinline__ Problem step_problem(const Problem &p, int k) {
     return q;
 }
 
+// One decode step (ssd_step): one token per (batch, head), state updated in place.
+struct StepArgs {
+    int batch, H, P, N, G, dtype;
+    const void *x;       // [batch, H, P] act
+    const void *dt;      // [batch, H] act
+    const void *B;       // [batch, G, N] act
+    const void *C;       // [batch, G, N] act
+    const float *A;      // [H]
+    const float *D;      // [H] or null
+    float *state;        // [batch, H, P, N]
+    void *y;             // [batch, H, P] act
+    uint32_t flags;
+};
+
+hipError_t launch_ssd_step(const StepArgs &a, hipStream_t s);
+bool step_supported(int dstate);
 hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_state(const Problem &p, hipStream_t s);
 hipError_t launch_state_pass(const Problem &p, hipStream_t s);

@@ -23,7 +23,7 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ER
 # Every symbol the header declares.
 EXPORTS = ["ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_segmented_workspace_bytes",
            "ssd_chunk_scan_segmented", "ssd_chunk_scan_stages", "ssd_workspace_layout",
-           "ssd_shape_supported", "ssd_status_string", "ssd_last_error_message", "ssd_version"]
+           "ssd_shape_supported", "ssd_status_string", "ssd_last_error_message", "ssd_version", "ssd_step"]
 
 
 class Dims(ctypes.Structure):
@@ -61,6 +61,8 @@ def lib():
         L.ssd_segmented_workspace_bytes.restype = sz
         L.ssd_chunk_scan_segmented.argtypes = [dp, i32, i64, vp, vp, vp, vp, vp, vp, vp, i32, u32, vp, vp, sz, vp]
         L.ssd_chunk_scan_segmented.restype = ctypes.c_int
+        L.ssd_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp]
+        L.ssd_step.restype = ctypes.c_int
         L.ssd_workspace_layout.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_workspace_layout.restype = ctypes.c_int
         L.ssd_shape_supported.argtypes = [i32, i32, i64, i64]
@@ -179,6 +181,21 @@ def horizontal(x0, dt, A, B, C, D, layer_states, chunk=256, *, residual=True, st
             final_state=layer_states[l], residual=residual, workspace=ws, stream=stream)
         u = out
     return u.clone(), layer_states
+
+
+def step(x, dt, A, B, C, D, state, *, y=None, residual=False, stream=None):
+    """One decode step (ssd_step): x [b, H, P], dt [b, H], B/C [b, G, N]; state [b, H, P, N]
+    float32 is updated in place.  Returns y [b, H, P]."""
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dtype = SSD_BF16 if x.dtype == torch.bfloat16 else SSD_F32
+    dims = Dims(b, 1, H, P, N, G, dtype, 0)
+    if y is None:
+        y = torch.empty_like(x)
+    flags = SSD_FLAG_RESIDUAL if residual else 0
+    _check(lib().ssd_step(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                          _ptr(state), _ptr(y), flags, _stream(stream)))
+    return y
 
 
 def tile_order_to_pn(t, P, N):

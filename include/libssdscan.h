@@ -161,6 +161,26 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
                                       void *y, void *workspace, size_t workspace_bytes,
                                       void *stream);
 
+/* One decode step: the next token of the recurrence of [分块推理 §2], continuing from
+ * a carried state (for example the final_state of a chunked prefill), as the per-layer
+ * fixed-size state of [分块推理 §2.3] is kept between tokens during generation:
+ *     a = exp(dt[b,h] A[h]);   state = a state + x (outer) B;
+ *     y[b,h,p] = sum_n C[b,g,n] state[b,h,p,n] + D[h] x[b,h,p]   (+ x with SSD_FLAG_RESIDUAL)
+ *   dims        shape of one layer; dims.seqlen must be 1.
+ *   x           [batch, nheads, headdim] (act), the token's input.
+ *   dt          [batch, nheads] (act).
+ *   A, D        [nheads] float32; D may be NULL.
+ *   B, C        [batch, ngroups, dstate] (act).
+ *   state       [batch, nheads, headdim, dstate] float32, read and written in place.
+ *   y           [batch, nheads, headdim] (act); must not overlap x or state.
+ *   flags       0 or SSD_FLAG_RESIDUAL.
+ * dstate must be one of 16, 32, 64, 128, 256; any headdim >= 1.  Alignment: state, B and
+ * C 16 bytes; x, dt, y their element size; A and D 4 bytes.  No workspace; nothing is
+ * allocated.  Returns SSD_OK once the kernel is enqueued on `stream`. */
+ssd_status_t ssd_step(const ssd_dims_t *dims, const void *x, const void *dt, const float *A,
+                      const void *B, const void *C, const float *D, float *state, void *y,
+                      uint32_t flags, void *stream);
+
 /* ---- inspection (tests and tools) ------------------------------------------------ */
 
 /* Runs steps first_stage..last_stage of ssd_chunk_scan_fwd (1 = log-decay prefix sums,

@@ -136,3 +136,26 @@ def test_tile_order_reindex_is_a_permutation():
     # tile (nt=1, pt=0), lane 17 (g=1, col=1), r=2 -> p=1, n=16+4+2
     idx = ((1 * (P // 16) + 0) * 64 + 17) * 4 + 2
     assert m[1, 22].item() == idx
+
+
+def test_step_argument_errors():
+    """ssd_step validates on the host; every call here fails before anything is enqueued."""
+    L = _lib()
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+
+    def step(dims, x=FAKE, dt=FAKE + 2 ** 30, A=FAKE + 2 ** 31, B=FAKE + 2 ** 32, C=FAKE + 2 ** 33, D=None,
+             state=FAKE + 2 ** 34, y=FAKE + 2 ** 35, flags=0):
+        dp = None if dims is None else ctypes.byref(dims)
+        return L.ssd_step(dp, v(x), v(dt), v(A), v(B), v(C), v(D), v(state), v(y), flags, None)
+    assert step(None) == 1
+    assert step(_dims(L=1, dtype=5)) == 3
+    assert step(_dims(L=2)) == 2                       # one token per call
+    assert step(_dims(L=1, H=3, G=2)) == 2
+    assert step(_dims(L=1, N=48)) == 4                 # dstate not in {16, 32, 64, 128, 256}
+    assert step(_dims(L=1), state=None) == 1
+    assert step(_dims(L=1), y=None) == 1
+    assert step(_dims(L=1), state=FAKE + 2 ** 34 + 8) == 5
+    assert step(_dims(L=1, dtype=1), x=FAKE + 1) == 5  # bf16 x must be 2-byte aligned
+    assert step(_dims(L=1), y=FAKE + 2 ** 34 + 64) == 8   # y inside state
+    assert step(_dims(L=1), flags=2) == 2
+    assert L.ssd_last_error_message().decode() != ""
