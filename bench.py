@@ -13,6 +13,7 @@ Besides the headline tokens/s the line carries:
                 runs on, inside full steps) against the 8 TB/s peak;
   kernels       the same figures for all four kernels, plus matrix-core rates;
   end_to_end    the method's bytes / step time against peak HBM bandwidth;
+  decode        the decode step (ssd_step) at the same layer shape, batch 1 and 8;
   stack         the 24-layer vertical stack (segmented entry point, wavefront and one
                 step at a time, and the horizontal order), a secondary figure;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores on the same inputs.
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the secondary timing of the 24-layer vertical stack")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the secondary timing of the decode step")
     ap.add_argument("--kernel-steps", type=int, default=0, help="launches per kernel for per-kernel timing "
                     "(default: --steps)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -155,6 +158,39 @@ def stack_timing(torch, dev, reps=5):
         ms = e0.elapsed_time(e1) / reps
         out["ms_" + name] = round(ms, 3)
         out["layer_tokens_per_s_" + name] = round(w.layers * w.tokens / (ms * 1e-3), 1)
+    return out
+
+
+def decode_timing(torch, dev, steps=200):
+    """ssd_step at the 128K-token layer's shape (H 48, P 64, N 128, bf16) at batch 1 and 8:
+    HIP events around `steps` consecutive steps on the same state.  A step must read and
+    write the fp32 state once (its HBM roofline); the rest of its traffic is a few KB."""
+    from chunked_linear_recurrence_amd import inputs, ssd
+    out = []
+    for b in (1, 8):
+        d = inputs.make_layer(b, steps, 48, 64, 128, 1, "bf16", seed=b, init="normal", init_std=0.5,
+                              dt_max=1e-2)
+        g = {k: v.to(dev) for k, v in d.items()}
+        toks = [(g["x"][:, t].contiguous(), g["dt"][:, t].contiguous(), g["B"][:, t].contiguous(),
+                 g["C"][:, t].contiguous()) for t in range(steps)]
+        state = g["init_state"].clone()
+        y = torch.empty_like(toks[0][0])
+        stream = torch.cuda.current_stream()
+        for t in range(10):
+            ssd.step(*toks[t][:2], g["A"], *toks[t][2:], g["D"], state, y=y, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(steps):
+            x, dt, B, C = toks[t]
+            ssd.step(x, dt, g["A"], B, C, g["D"], state, y=y, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        sbytes = 2 * state.numel() * 4
+        out.append({"batch": b, "nheads": 48, "headdim": 64, "dstate": 128, "us_per_step": round(us, 2),
+                    "tokens_per_s": round(b / (us * 1e-6), 1), "state_bytes_per_step": sbytes,
+                    "state_GB_s": round(sbytes / (us * 1e-6) / 1e9, 1)})
     return out
 
 
@@ -281,6 +317,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+    if not args.no_decode:
+        print("[bench] decode step", file=sys.stderr, flush=True)
+        out["decode"] = decode_timing(torch, dev)
     if not args.no_stack:
         print("[bench] vertical stack", file=sys.stderr, flush=True)
         out["stack"] = stack_timing(torch, dev)
