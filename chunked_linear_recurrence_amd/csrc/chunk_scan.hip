@@ -343,19 +343,24 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
                 dma16(sv + ((kk * NW + w) * 64 + lane) * 16, buf + Buf::O_ST + (kk * NW + w) * 1024);
             }
         } else {
+            // cum, F and G of one (head, chunk) are CP and FP 16-byte pieces, which need not
+            // fill whole waves (Q < 256): the guard is per lane, so no lane reads past the
+            // row or writes past its LDS region
             const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
-            if (w * 64 < CP)
-                dma16(reinterpret_cast<const unsigned char *>(reinterpret_cast<const S *>(p.dA_cum) + tok) +
-                          (w * 64 + lane) * 16, buf + Buf::O_CM + w * 1024);
-            if (w * 64 < FP) {
-                dma16(reinterpret_cast<const unsigned char *>(p.decF + tok) + (w * 64 + lane) * 16,
-                      buf + Buf::O_F + w * 1024);
-                dma16(reinterpret_cast<const unsigned char *>(p.decG + tok) + (w * 64 + lane) * 16,
-                      buf + Buf::O_G + w * 1024);
+            const int pc = w * 64 + lane;
+            if (pc < CP)
+                dma16(reinterpret_cast<const unsigned char *>(reinterpret_cast<const S *>(p.dA_cum) + tok) + pc * 16,
+                      buf + Buf::O_CM + w * 1024);
+            if (pc < FP) {
+                dma16(reinterpret_cast<const unsigned char *>(p.decF + tok) + pc * 16, buf + Buf::O_F + w * 1024);
+                dma16(reinterpret_cast<const unsigned char *>(p.decG + tok) + pc * 16, buf + Buf::O_G + w * 1024);
             }
         }
     };
     static_assert(CP <= THREADS && FP <= THREADS, "cum/F/G fit one DMA item");
+    // the x, state and B pieces always fill whole waves, so their guards are uniform
+    static_assert((Q * XPIECES) % 64 == 0 && SP % 64 == 0 && (Q * Cfg::BPIECES) % 64 == 0,
+                  "x, state and B tiles are whole waves of 16-byte pieces");
 
     T *ychunk = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)t0 * HP;
     unsigned char *ys = smem + (Cfg::DB ? 2 : 1) * Buf::BYTES + (Cfg::YS ? w * Cfg::YW : 0);

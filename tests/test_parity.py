@@ -197,3 +197,21 @@ def test_narrow_dt_variant():
     yr, fr = oracle_layer(d)
     assert err_bf16(y, yr) <= 2e-2
     assert err_bf16(fin, fr) <= 2e-2
+
+
+@pytest.mark.parametrize("Q", [64, 128])
+def test_long_context_smaller_chunks(Q):
+    """The 128K-token layer with Q = 64 and 128 (2048 and 1024 chunks): sampled heads over
+    the whole sequence.  For Q < 256 a chunk's decay rows are less than one wave of 16-byte
+    pieces, and the per-lane guard on their DMA keeps every read inside the workspace
+    (whose end coincides with the allocation's at this size)."""
+    w = WORKLOADS["long_context_b1_L131072_h48"]
+    d = inputs.make(w)
+    y, fin = run_gpu(d, Q)
+    A = d["A"].numpy()
+    heads = sorted({int(np.argmax(A)), int(np.argmin(A)), 7})
+    sub = dict(x=d["x"][:, :, heads], dt=d["dt"][:, :, heads], A=d["A"][heads], B=d["B"],
+               C=d["C"], D=d["D"][heads], init_state=None)
+    yr, fr = oracle_layer(sub)
+    assert err_bf16(y[:, :, heads], yr) <= 2e-2
+    assert err_bf16(fin[:, heads], fr) <= 2e-2
