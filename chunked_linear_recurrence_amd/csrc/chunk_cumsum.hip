@@ -46,7 +46,9 @@ __device__ __forceinline__ void store_run(V *dst, const V (&v)[E]) {
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
     typedef typename CumT<T>::type S;
-    constexpr int E = Q / 64;                    // values per lane
+    constexpr int E = Q >= 64 ? Q / 64 : 1;      // values per lane
+    constexpr int NA = Q / E;                    // lanes holding tokens (64, or Q when Q < 64)
+    static_assert(16 % E == 0 && NA <= 64, "a lane's tokens lie in one 16-token block");
     __shared__ S tile[kCumHeads][Q + 1];
     const int c = blockIdx.x, hb = blockIdx.y * kCumHeads, b = blockIdx.z % p0.batch;
     const Problem p = step_problem(p0, blockIdx.z / p0.batch);
@@ -65,11 +67,15 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool active = lane < NA;
     for (int hh = wave; hh < nh; hh += 4) {
         S v[E];
         S run = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) { run += tile[hh][lane * E + e]; v[e] = run; }
+        for (int e = 0; e < E; ++e) {
+            if (active) run += tile[hh][lane * E + e];
+            v[e] = run;
+        }
         // inclusive scan of the lane totals across the wave
         S incl = run;
 #pragma unroll
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
         S cv[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) cv[e] = (lane * E + e <= last) ? excl + v[e] : lastv;
-        store_run<S, E>(out, cv);
+        if (active) store_run<S, E>(out, cv);
         // block end of this lane's tokens (E divides 16, so they share one block)
         const int src = ((lane * E) / 16 * 16 + 15) / E;
         const S cend = __shfl(cv[E - 1], src, 64);
@@ -103,20 +109,24 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
             fv[e] = expf((float)(cend - cv[e]));
             gv[e] = expf((float)cv[e]);
         }
-        store_run<float, E>(p.decF + fo, fv);
-        store_run<float, E>(p.decG + fo, gv);
+        if (active) {
+            store_run<float, E>(p.decF + fo, fv);
+            store_run<float, E>(p.decG + fo, gv);
+        }
     }
 }
 
 hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s) {
     dim3 grid(p.nc, (p.H + kCumHeads - 1) / kCumHeads, p.batch * step_count(p));
     if (p.dtype == 1) {
-        if (p.Q == 64) chunk_cumsum_kernel<bf16, 64><<<grid, 256, 0, s>>>(p);
+        if (p.Q == 32) chunk_cumsum_kernel<bf16, 32><<<grid, 256, 0, s>>>(p);
+        else if (p.Q == 64) chunk_cumsum_kernel<bf16, 64><<<grid, 256, 0, s>>>(p);
         else if (p.Q == 128) chunk_cumsum_kernel<bf16, 128><<<grid, 256, 0, s>>>(p);
         else if (p.Q == 256) chunk_cumsum_kernel<bf16, 256><<<grid, 256, 0, s>>>(p);
         else return hipErrorInvalidValue;
     } else {
-        if (p.Q == 64) chunk_cumsum_kernel<float, 64><<<grid, 256, 0, s>>>(p);
+        if (p.Q == 32) chunk_cumsum_kernel<float, 32><<<grid, 256, 0, s>>>(p);
+        else if (p.Q == 64) chunk_cumsum_kernel<float, 64><<<grid, 256, 0, s>>>(p);
         else if (p.Q == 128) chunk_cumsum_kernel<float, 128><<<grid, 256, 0, s>>>(p);
         else if (p.Q == 256) chunk_cumsum_kernel<float, 256><<<grid, 256, 0, s>>>(p);
         else return hipErrorInvalidValue;

@@ -57,7 +57,7 @@ struct ScanCfg {
     static constexpr int BPIECES = N * (int)sizeof(T) / 16;      // 16-byte pieces per B row
     static constexpr bool BL = DB && Q * N * (int)sizeof(T) <= LDS - HEAD_BYTES;
     static constexpr bool OK = LDS <= kLdsBytes &&
-                               (sizeof(T) == 4 || NT % 2 == 0) && (Q == 64 || Q == 128 || Q == 256) &&
+                               (sizeof(T) == 4 || NT % 2 == 0) && (Q == 32 || Q == 64 || Q == 128 || Q == 256) &&
                                P * (int)sizeof(T) >= 32;
 };
 
@@ -541,6 +541,7 @@ static hipError_t launch_scan_t(const Problem &p, hipStream_t s) {
 }
 
 #define SSD_SCAN_SHAPES(X, T)                                                              \
+    X(T, 32, 32, 64) X(T, 32, 64, 64) X(T, 32, 64, 128)                                    \
     X(T, 64, 16, 16) X(T, 64, 16, 32) X(T, 64, 16, 64) X(T, 64, 16, 128)                   \
     X(T, 64, 32, 32) X(T, 64, 32, 64) X(T, 64, 32, 128) X(T, 64, 64, 64) X(T, 64, 64, 128) \
     X(T, 128, 32, 64) X(T, 128, 64, 64) X(T, 128, 64, 128)                                 \

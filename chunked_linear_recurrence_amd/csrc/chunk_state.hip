@@ -234,6 +234,7 @@ static hipError_t launch_state_t(const Problem &p, hipStream_t s) {
 }
 
 #define SSD_STATE_SHAPES(X, T)                                                             \
+    X(T, 32, 32, 64) X(T, 32, 64, 64) X(T, 32, 64, 128)                                    \
     X(T, 64, 16, 16) X(T, 64, 16, 32) X(T, 64, 16, 64) X(T, 64, 16, 128)                   \
     X(T, 64, 32, 32) X(T, 64, 32, 64) X(T, 64, 32, 128) X(T, 64, 64, 64) X(T, 64, 64, 128) \
     X(T, 128, 32, 64) X(T, 128, 64, 64) X(T, 128, 64, 128)                                 \

@@ -47,7 +47,7 @@
  *   aligned; A and D 4-byte aligned; dt aligned to its element size.
  *
  * Supported shapes on the GPU path (others return SSD_ERR_UNSUPPORTED):
- *   chunk_Q in {64, 128, 256}; headdim in {16, 32, 64, 128}; dstate in {16, 32, 64, 128,
+ *   chunk_Q in {32, 64, 128, 256}; headdim in {16, 32, 64, 128}; dstate in {16, 32, 64, 128,
  *   256} (bfloat16 needs dstate >= 32); the set actually compiled is reported by
  *   ssd_shape_supported().  Any batch, seqlen >= 1, nheads >= 1 with nheads % ngroups == 0.
  *   A must be finite.  The last chunk may be shorter than Q.

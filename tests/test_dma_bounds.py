@@ -9,7 +9,7 @@ import pytest
 
 LDS_MAX = 160 * 1024
 # (Q, P, N) compiled for chunk_scan (SSD_SCAN_SHAPES)
-SHAPES = [(64, 16, 16), (64, 16, 32), (64, 16, 64), (64, 16, 128), (64, 32, 32), (64, 32, 64), (64, 32, 128),
+SHAPES = [(32, 32, 64), (32, 64, 64), (32, 64, 128), (64, 16, 16), (64, 16, 32), (64, 16, 64), (64, 16, 128), (64, 32, 32), (64, 32, 64), (64, 32, 128),
           (64, 64, 64), (64, 64, 128), (128, 32, 64), (128, 64, 64), (128, 64, 128), (256, 16, 32),
           (256, 32, 64), (256, 64, 64), (256, 64, 128), (256, 128, 128), (256, 64, 256)]
 

@@ -215,3 +215,31 @@ def test_long_context_smaller_chunks(Q):
     yr, fr = oracle_layer(sub)
     assert err_bf16(y[:, :, heads], yr) <= 2e-2
     assert err_bf16(fin[:, heads], fr) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("P,N", [(32, 64), (64, 64), (64, 128)])
+def test_chunk_length_32(dtype, P, N):
+    """Q = 32 (the smallest chunk the pages list, for other model families): several chunks,
+    a ragged tail, two groups, a nonzero initial state."""
+    d = small(2, 5 * 32 + 11, 4, P, N, 2, dtype, seed=P + N)
+    y, fin = run_gpu(d, 32)
+    yr, fr = oracle_layer(d)
+    err = err_for(dtype)
+    assert err(y, yr) <= tol_for(dtype)
+    assert err(fin, fr) <= tol_for(dtype)
+
+
+def test_head_grouping_does_not_change_the_result(monkeypatch):
+    """Heads per workgroup only split the work: every split gives bit-identical outputs
+    (ngroups 4, heads per group 3, so some splits leave a short last group)."""
+    d = small(2, 700, 12, 64, 128, 4, "bf16", seed=21)
+    outs = []
+    for hs, hc in (("1", "1"), ("2", "3"), ("3", "2"), ("64", "64")):
+        monkeypatch.setenv("SSD_HEADS_PER_WG_STATE", hs)
+        monkeypatch.setenv("SSD_HEADS_PER_WG_SCAN", hc)
+        outs.append(run_gpu(d, 256))
+    for y, fin in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(fin, outs[0][1])
+    yr, fr = oracle_layer(d)
+    assert err_bf16(outs[0][0], yr) <= 2e-2

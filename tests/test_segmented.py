@@ -134,3 +134,20 @@ def test_vertical_stack_workload():
                                        d["C"], d["D"][:, [h]])
     assert err_bf16(y_seg[:, :, [h]], yr1) <= 2e-2
     assert err_bf16(s_seg[:, :, [h]], fr1) <= 2e-2
+
+
+def test_wavefront_chunk_length_32_and_groups():
+    """The stack at Q = 32 with two B/C groups: wavefront == one step at a time == horizontal."""
+    nl, b, L, H, P, N, Q, V = 4, 1, 600, 4, 64, 64, 32, 96
+    d = inputs.make_stack(b, L, H, P, N, 2, nl, "bf16", seed=5)
+    g = to_dev(d, DEV)
+    s1 = torch.zeros(nl, b, H, P, N, device=DEV)
+    s2, s3 = s1.clone(), s1.clone()
+    y1, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s1, V, Q, wavefront=True)
+    y2, _ = ssd.segmented(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s2, V, Q, wavefront=False)
+    y3, _ = ssd.horizontal(g["x0"], g["dt"], g["A"], g["B"], g["C"], g["D"], s3, Q)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    assert torch.equal(s1, s2) and torch.equal(s1, s3)
+    yr, fr = oracle.stack_horizontal(d["x0"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    assert err_bf16(y1, yr) <= 2e-2
