@@ -1,0 +1,192 @@
+// chunk_scan_assoc: the chunk outputs of [分块推理 §2.1-§2.2] (page
+// "分块推理：解锁循环模型并行计算，实现长序列高效处理") computed in the scan form the page
+// describes for the intra-chunk part: within a chunk the recurrence h_t = a_t h_{t-1} +
+// x_t (outer) B_t is a prefix computation over the associative pairs (a_t, x_t B_t), with
+// (a1, v1) then (a2, v2) combining to (a1 a2, a2 v1 + v2), so it can be evaluated as a
+// log-depth tree.  This kernel is the alternative to chunk_scan's matrix-core form (same
+// inputs, same outputs); it exists to measure that choice.
+//
+// One workgroup per (batch, chunk, head), one wave per window of 64 tokens, lane = token.
+// For each state element (p, n):
+//   - every lane forms v_t = x_t[p] B_t[n] and the wave runs an inclusive tree scan over
+//     its 64 tokens in log2(64) = 6 shuffle steps (span 1, 2, 4, ..., 32), the step of span
+//     d multiplying the partner's value by the decay exp(cum_t - cum_{t-d}) (per lane,
+//     computed once from the chunk's dA_cum row);
+//   - lane 63 leaves its window's end value in LDS; the state entering window w is then
+//     exp(cum_{64w-1}) b_in + sum_{w' < w} exp(cum_{64w-1} - cum_{64w'+63}) end_{w'}
+//     (the top levels of the tree, across the chunk's Q/64 windows), and reaches token t
+//     with the factor exp(cum_t - cum_{64w-1});
+//   - y_t[p] accumulates C_t[n] h_t[n] over n in a register.
+// y_t = sum_n C_t[n] h_t[n] + (D + residual) x_t, rounded once to the activation dtype.
+// B and C of the chunk are staged once in LDS with one padding word per row, so the 64
+// lanes (64 different rows) read different banks.
+#include "ssd_common.h"
+
+namespace ssd {
+
+template <typename T, int Q, int N>
+struct AssocCfg {
+    static constexpr int NWIN = Q >= 64 ? Q / 64 : 1;           // waves (64-token windows)
+    static constexpr int THREADS = NWIN * 64;
+    static constexpr int EPW = 4 / (int)sizeof(T);             // elements per 4-byte word
+    static constexpr int WPR = N / EPW;                         // words per row
+    static constexpr int RSW = WPR + 1;                         // LDS row stride in words
+    static constexpr int TILE_BYTES = Q * RSW * 4;              // one of B, C
+    static constexpr int LDS = 2 * TILE_BYTES + 2 * NWIN * N * 4;
+    static constexpr bool OK = LDS <= kLdsBytes;
+};
+
+// Element e (0 .. EPW-1) of an LDS word.
+template <typename T>
+__device__ __forceinline__ float word_elem(uint32_t wd, int e);
+template <>
+__device__ __forceinline__ float word_elem<float>(uint32_t wd, int) { return __uint_as_float(wd); }
+template <>
+__device__ __forceinline__ float word_elem<bf16>(uint32_t wd, int e) {
+    return __uint_as_float(e ? (wd & 0xffff0000u) : (wd << 16));
+}
+
+// Element (p, n) of one P x N state stored in tile order (see libssdscan.h).
+__device__ __forceinline__ int64_t tile_index(int p, int n, int PT) {
+    return ((int64_t)((n >> 4) * PT + (p >> 4)) * 64 + ((p & 15) + 16 * ((n & 15) >> 2))) * 4 + (n & 3);
+}
+
+template <typename T, int Q, int P, int N>
+__global__ __launch_bounds__((AssocCfg<T, Q, N>::THREADS)) void chunk_scan_assoc_kernel(Problem p0) {
+    using Cfg = AssocCfg<T, Q, N>;
+    typedef typename CumT<T>::type S;
+    constexpr int NWIN = Cfg::NWIN, EPW = Cfg::EPW, WPR = Cfg::WPR, RSW = Cfg::RSW;
+    constexpr int PT = P / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *Bs = reinterpret_cast<uint32_t *>(smem);
+    uint32_t *Cs = Bs + Q * RSW;
+    float *endv = reinterpret_cast<float *>(Cs + Q * RSW);    // [2][NWIN][N]
+
+    const Problem p = step_problem(p0, blockIdx.y);
+    const int logical = blockIdx.x;                            // (b, c, h)
+    const int h = logical % p0.H;
+    const int bc = logical / p0.H;
+    const int c = bc % p0.nc, b = bc / p0.nc;
+    if (c >= p.nc) return;                                     // past a short last segment (uniform)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // window of this wave
+    const int t = w * 64 + lane;                               // token within the chunk
+    const int t0 = c * Q;
+    const int Qc = min(Q, p.L - t0);
+    const bool act = t < Qc;
+    const int g = h / (p.H / p.G);
+    const int64_t HP = (int64_t)p.H * P;
+
+    // B and C rows of the chunk -> LDS (zero past the chunk's last token)
+    {
+        const unsigned char *Bb = reinterpret_cast<const unsigned char *>(p.B) +
+                                  (((int64_t)b * p.bc_bs + (int64_t)t0 * p.G * N + (int64_t)g * N) * sizeof(T));
+        const unsigned char *Cb = reinterpret_cast<const unsigned char *>(p.C) +
+                                  (((int64_t)b * p.bc_bs + (int64_t)t0 * p.G * N + (int64_t)g * N) * sizeof(T));
+        const int64_t rowb = (int64_t)p.G * N * sizeof(T);
+        for (int idx = tid; idx < Q * WPR; idx += Cfg::THREADS) {
+            const int j = idx / WPR, k = idx % WPR;
+            uint32_t bw = 0, cw = 0;
+            if (j < Qc) {
+                bw = *reinterpret_cast<const uint32_t *>(Bb + j * rowb + k * 4);
+                cw = *reinterpret_cast<const uint32_t *>(Cb + j * rowb + k * 4);
+            }
+            Bs[j * RSW + k] = bw;
+            Cs[j * RSW + k] = cw;
+        }
+    }
+
+    // per-lane decay factors from the chunk's log-decay prefix sums
+    const S *cum = reinterpret_cast<const S *>(p.dA_cum) + (((int64_t)b * p.H + h) * p.nc + c) * Q;
+    const int tc = t < Q ? t : Q - 1;
+    const S ct = cum[tc];
+    const S cws = w > 0 ? cum[w * 64 - 1] : (S)0;             // sum before this window
+    const float Pw = __expf((float)(ct - cws));                // window start .. t
+    float M[6];                                                // tree step of span 2^s
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+        const int d = 1 << s;
+        // lane >= d and t < Q keep t - d inside the chunk's row
+        M[s] = (lane >= d && t < Q) ? __expf((float)(ct - cum[t - d >= 0 ? t - d : 0])) : 0.f;
+    }
+    const float Dwin = __expf((float)cws);                     // chunk start .. window start
+    float Dww[NWIN];                                           // end of window w' .. window start
+#pragma unroll
+    for (int v = 0; v < NWIN; ++v) Dww[v] = v < w ? __expf((float)(cws - cum[min(v * 64 + 63, Q - 1)])) : 0.f;
+    const float dres = (p.D ? p.D[h] : 0.f) + ((p.flags & 1u) ? 1.f : 0.f);
+    const T *xr = reinterpret_cast<const T *>(p.x) + (int64_t)b * p.x_bs + (int64_t)(t0 + (act ? t : 0)) * HP + h * P;
+    T *yr = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)(t0 + (act ? t : 0)) * HP + h * P;
+    const T *bin = reinterpret_cast<const T *>(p.b_in) + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)P * N;
+    __syncthreads();
+
+    for (int pp = 0, par = 0; pp < P; ++pp, par ^= 1) {
+        const float xv = act ? to_f32(xr[pp]) : 0.f;
+        float yl = 0.f;
+        float *ev = endv + (par * NWIN + w) * N;
+        for (int k = 0; k < WPR; ++k) {
+            const uint32_t bw = Bs[t < Q ? t * RSW + k : k];
+            const uint32_t cw = Cs[t < Q ? t * RSW + k : k];
+#pragma unroll
+            for (int e = 0; e < EPW; ++e) {
+                float v = t < Q ? xv * word_elem<T>(bw, e) : 0.f;
+#pragma unroll
+                for (int s = 0; s < 6; ++s) {                 // inclusive tree scan over the window
+                    const float u = __shfl_up(v, 1 << s, 64);
+                    if (lane >= (1 << s)) v = fmaf(M[s], u, v);
+                }
+                yl = fmaf(word_elem<T>(cw, e), v, yl);
+                if (lane == 63) ev[k * EPW + e] = v;
+            }
+        }
+        __syncthreads();                                        // every window's end values
+        // state entering this window, contracted with C_t
+        float yc = 0.f;
+        const float *e0 = endv + par * NWIN * N;
+        for (int n = 0; n < N; ++n) {
+            float K = Dwin * to_f32(bin[tile_index(pp, n, PT)]);
+#pragma unroll
+            for (int v = 0; v < NWIN; ++v)
+                if (v < w) K = fmaf(Dww[v], e0[v * N + n], K);
+            const uint32_t cw = Cs[(t < Q ? t : 0) * RSW + n / EPW];
+            yc = fmaf(word_elem<T>(cw, n % EPW), K, yc);
+        }
+        if (act) yr[pp] = from_f32<T>(fmaf(Pw, yc, yl) + dres * xv);
+    }
+}
+
+template <typename T, int Q, int P, int N>
+static hipError_t launch_assoc_t(const Problem &p, hipStream_t s) {
+    using Cfg = AssocCfg<T, Q, N>;
+    if constexpr (!Cfg::OK) {
+        return hipErrorInvalidValue;
+    } else {
+        static const hipError_t attr = hipFuncSetAttribute(
+            (const void *)chunk_scan_assoc_kernel<T, Q, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+        if (attr != hipSuccess) return attr;
+        const int64_t nblk = (int64_t)p.batch * p.nc * p.H;
+        if (nblk <= 0 || nblk > 0x7fffffff) return hipErrorInvalidValue;
+        chunk_scan_assoc_kernel<T, Q, P, N><<<dim3((unsigned)nblk, step_count(p)), Cfg::THREADS, Cfg::LDS, s>>>(p);
+        return hipGetLastError();
+    }
+}
+
+#define SSD_ASSOC_SHAPES(X, T) \
+    X(T, 32, 64, 64) X(T, 64, 32, 64) X(T, 64, 64, 64) X(T, 64, 64, 128) X(T, 128, 64, 128) X(T, 256, 64, 128)
+#define SSD_ASSOC_CASE(T, q, pp, nn) \
+    if (p.Q == q && p.P == pp && p.N == nn) return launch_assoc_t<T, q, pp, nn>(p, s);
+#define SSD_ASSOC_OK(T, q, pp, nn) \
+    if (Q == q && P == pp && N == nn) return AssocCfg<T, q, nn>::OK;
+
+hipError_t launch_chunk_scan_assoc(const Problem &p, hipStream_t s) {
+    if (p.dtype == 1) { SSD_ASSOC_SHAPES(SSD_ASSOC_CASE, bf16) }
+    else { SSD_ASSOC_SHAPES(SSD_ASSOC_CASE, float) }
+    return hipErrorInvalidValue;
+}
+
+bool chunk_scan_assoc_supported(int dtype, int Q, int P, int N) {
+    if (dtype == 1) { SSD_ASSOC_SHAPES(SSD_ASSOC_OK, bf16) }
+    else { SSD_ASSOC_SHAPES(SSD_ASSOC_OK, float) }
+    return false;
+}
+
+}  // namespace ssd

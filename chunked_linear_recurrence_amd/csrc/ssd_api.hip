@@ -165,7 +165,8 @@ ssd_status_t run_layer(const ssd::Problem &p, hipStream_t s, int first_stage, in
         return fail(SSD_ERR_HIP, "chunk_state launch failed: %s", hipGetErrorString(e));
     if (in(3) && (e = ssd::launch_state_pass(p, s)) != hipSuccess)
         return fail(SSD_ERR_HIP, "state_pass launch failed: %s", hipGetErrorString(e));
-    if (in(4) && (e = ssd::launch_chunk_scan(p, s)) != hipSuccess)
+    if (in(4) && (e = (p.flags & SSD_FLAG_SCAN_FORM) ? ssd::launch_chunk_scan_assoc(p, s)
+                                                      : ssd::launch_chunk_scan(p, s)) != hipSuccess)
         return fail(SSD_ERR_HIP, "chunk_scan launch failed: %s", hipGetErrorString(e));
     return SSD_OK;
 }
@@ -179,7 +180,10 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     const ssd_dims_t &d = *dims;
     if (!x || !dt || !A || !B || !C || !y)
         return fail(SSD_ERR_NULL_ARG, "x, dt, A, B, C and y must be non-NULL");
-    if (flags & ~SSD_FLAG_RESIDUAL) return fail(SSD_ERR_BAD_SHAPE, "unknown flag bits 0x%x", flags);
+    if (flags & ~(SSD_FLAG_RESIDUAL | SSD_FLAG_SCAN_FORM)) return fail(SSD_ERR_BAD_SHAPE, "unknown flag bits 0x%x", flags);
+    if ((flags & SSD_FLAG_SCAN_FORM) && !ssd::chunk_scan_assoc_supported(d.dtype, chunk_Q, (int)d.headdim, (int)d.dstate))
+        return fail(SSD_ERR_UNSUPPORTED, "no scan-form kernel for dtype %d chunk_Q %d headdim %lld dstate %lld",
+                    d.dtype, chunk_Q, (long long)d.headdim, (long long)d.dstate);
     if (st = check_alignment(x, dt, A, B, C, D, init_state, y, final_state, workspace, d.dtype); st != SSD_OK)
         return st;
     Layout lo;
@@ -225,6 +229,12 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
 }  // namespace
 
 extern "C" {
+
+int32_t ssd_scan_form_supported(int32_t dtype, int32_t chunk_Q, int64_t headdim, int64_t dstate) {
+    if (dtype != SSD_F32 && dtype != SSD_BF16) return 0;
+    if (headdim > 1024 || dstate > 1024 || !ssd_shape_supported(dtype, chunk_Q, headdim, dstate)) return 0;
+    return ssd::chunk_scan_assoc_supported(dtype, chunk_Q, (int)headdim, (int)dstate);
+}
 
 int32_t ssd_shape_supported(int32_t dtype, int32_t chunk_Q, int64_t headdim, int64_t dstate) {
     if (dtype != SSD_F32 && dtype != SSD_BF16) return 0;

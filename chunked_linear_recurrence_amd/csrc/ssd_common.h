@@ -152,6 +152,8 @@ hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_state(const Problem &p, hipStream_t s);
 hipError_t launch_state_pass(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_scan(const Problem &p, hipStream_t s);
+hipError_t launch_chunk_scan_assoc(const Problem &p, hipStream_t s);
+bool chunk_scan_assoc_supported(int dtype, int Q, int P, int N);
 bool chunk_state_supported(int dtype, int Q, int P, int N);
 bool chunk_scan_supported(int dtype, int Q, int P, int N);
 

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "_build", "libssdscan.so")
 SSD_F32, SSD_BF16 = 0, 1
 SSD_FLAG_RESIDUAL = 1
 SSD_FLAG_WAVEFRONT = 2
+SSD_FLAG_SCAN_FORM = 4
 
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_BAD_DTYPE",
           4: "SSD_ERR_UNSUPPORTED", 5: "SSD_ERR_MISALIGNED", 6: "SSD_ERR_WORKSPACE",
@@ -23,7 +24,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ER
 # Every symbol the header declares.
 EXPORTS = ["ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_segmented_workspace_bytes",
            "ssd_chunk_scan_segmented", "ssd_chunk_scan_stages", "ssd_workspace_layout",
-           "ssd_shape_supported", "ssd_status_string", "ssd_last_error_message", "ssd_version", "ssd_step"]
+           "ssd_shape_supported", "ssd_status_string", "ssd_last_error_message", "ssd_version", "ssd_step",
+           "ssd_scan_form_supported"]
 
 
 class Dims(ctypes.Structure):
@@ -65,6 +67,8 @@ def lib():
         L.ssd_step.restype = ctypes.c_int
         L.ssd_workspace_layout.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_workspace_layout.restype = ctypes.c_int
+        L.ssd_scan_form_supported.argtypes = [i32, i32, i64, i64]
+        L.ssd_scan_form_supported.restype = i32
         L.ssd_shape_supported.argtypes = [i32, i32, i64, i64]
         L.ssd_shape_supported.restype = i32
         L.ssd_status_string.argtypes = [ctypes.c_int]
@@ -104,6 +108,10 @@ def shape_supported(dtype, chunk, headdim, dstate) -> bool:
     return bool(lib().ssd_shape_supported(dtype, chunk, headdim, dstate))
 
 
+def scan_form_supported(dtype, chunk, headdim, dstate) -> bool:
+    return bool(lib().ssd_scan_form_supported(dtype, chunk, headdim, dstate))
+
+
 def workspace_bytes(dims, chunk) -> int:
     return lib().ssd_chunk_scan_workspace_bytes(ctypes.byref(dims), chunk)
 
@@ -127,8 +135,10 @@ def alloc_workspace(nbytes, device):
 
 
 def fwd(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y=None, final_state=None,
-        residual=False, workspace=None, stream=None, want_final=True, first_stage=1, last_stage=NSTAGES):
-    """One layer over the whole sequence (ssd_chunk_scan_fwd).  Returns (y, final_state)."""
+        residual=False, workspace=None, stream=None, want_final=True, first_stage=1, last_stage=NSTAGES,
+        scan_form=False):
+    """One layer over the whole sequence (ssd_chunk_scan_fwd).  Returns (y, final_state).
+    scan_form=True computes the chunk outputs with the associative-scan kernel."""
     dims = dims_of(x, B)
     nbytes = workspace_bytes(dims, chunk)
     if nbytes == 0:
@@ -141,7 +151,7 @@ def fwd(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y=None, final_sta
     if final_state is None and want_final:
         final_state = torch.empty(x.shape[0], x.shape[2], x.shape[3], B.shape[3], dtype=torch.float32,
                                   device=x.device)
-    flags = SSD_FLAG_RESIDUAL if residual else 0
+    flags = (SSD_FLAG_RESIDUAL if residual else 0) | (SSD_FLAG_SCAN_FORM if scan_form else 0)
     args = (ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
             chunk, _ptr(y), _ptr(final_state), flags, _ptr(workspace), workspace.numel(), _stream(stream))
     if first_stage == 1 and last_stage == NSTAGES:

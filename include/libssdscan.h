@@ -97,6 +97,12 @@ typedef struct ssd_dims {
 #define SSD_FLAG_RESIDUAL 1u   /* y = (recurrence output + D x) + x, rounded once to act */
 #define SSD_FLAG_WAVEFRONT 2u  /* segmented stack only: run independent (segment, layer)
                                   steps together (see ssd_chunk_scan_segmented) */
+#define SSD_FLAG_SCAN_FORM 4u  /* ssd_chunk_scan_fwd / _stages only: compute the chunk outputs
+                                  with the associative-scan form of [分块推理 §2.1] (a
+                                  log-depth tree over the pairs (a_t, x_t B_t) on the vector
+                                  units) instead of the matrix-core form; same results within
+                                  the tolerances, for comparison.  Shapes:
+                                  ssd_scan_form_supported(). */
 
 /* Size in bytes of the workspace ssd_chunk_scan_fwd needs for these dims and chunk_Q,
  * or 0 when the arguments are invalid.  The workspace holds the per-chunk log-decay
@@ -110,7 +116,7 @@ size_t ssd_chunk_scan_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q);
  *   y                  output [batch, seqlen, nheads, headdim] (act); must not overlap x.
  *   final_state        state after the last token, or NULL; may be the same pointer as
  *                      init_state (updated in place), no other overlap allowed.
- *   flags              0 or SSD_FLAG_RESIDUAL.
+ *   flags              0, SSD_FLAG_RESIDUAL and/or SSD_FLAG_SCAN_FORM.
  *   workspace          caller-owned device scratch; its contents on entry do not matter.
  * Returns SSD_OK once the kernels are enqueued on `stream`. */
 ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, const void *x, const void *dt,
@@ -208,6 +214,9 @@ ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const 
  * x 4 values, where lane l, value r holds (p = 16 * (p / 16) + l % 16,
  * n = 16 * (n / 16) + 4 * (l / 16) + r). */
 ssd_status_t ssd_workspace_layout(const ssd_dims_t *dims, int32_t chunk_Q, size_t offsets[4]);
+
+/* 1 when the SSD_FLAG_SCAN_FORM kernel is compiled for (dtype, chunk_Q, headdim, dstate). */
+int32_t ssd_scan_form_supported(int32_t dtype, int32_t chunk_Q, int64_t headdim, int64_t dstate);
 
 /* 1 when a compiled kernel set covers (dtype, chunk_Q, headdim, dstate), else 0. */
 int32_t ssd_shape_supported(int32_t dtype, int32_t chunk_Q, int64_t headdim, int64_t dstate);

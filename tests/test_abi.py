@@ -159,3 +159,19 @@ def test_step_argument_errors():
     assert step(_dims(L=1), y=FAKE + 2 ** 34 + 64) == 8   # y inside state
     assert step(_dims(L=1), flags=2) == 2
     assert L.ssd_last_error_message().decode() != ""
+
+
+def test_scan_form_flag_validation():
+    """SSD_FLAG_SCAN_FORM is accepted by the layer entry points only, for the shapes its
+    kernel is compiled for."""
+    L = _lib()
+    assert ssd.scan_form_supported(1, 256, 64, 128)
+    assert not ssd.scan_form_supported(1, 256, 64, 256)      # B and C tiles would not fit LDS
+    assert not ssd.scan_form_supported(0, 256, 64, 128)
+    assert _fwd(_dims(P=64, N=256, dtype=1), Q=256, flags=4) == 4
+    assert _fwd(_dims(P=64, N=128, dtype=1), Q=256, flags=8) == 2  # unknown bit
+    d = _dims(L=512)
+    v = ctypes.c_void_p
+    assert L.ssd_chunk_scan_segmented(ctypes.byref(d), 2, 128, v(FAKE), v(FAKE + 2 ** 30), v(FAKE + 2 ** 31),
+                                      v(FAKE + 2 ** 32), v(FAKE + 2 ** 33), None, v(FAKE + 2 ** 36), 64, 4,
+                                      v(FAKE + 2 ** 34), v(FAKE + 2 ** 35), 1 << 30, None) == 2
