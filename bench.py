@@ -13,6 +13,8 @@ Besides the headline tokens/s the line carries:
                 runs on, inside full steps) against the 8 TB/s peak;
   kernels       the same figures for all four kernels, plus matrix-core rates;
   end_to_end    the method's bytes / step time against peak HBM bandwidth;
+  scan_form     the chunk outputs computed by the associative-scan kernel instead of the
+                matrix-core one (same layer), for comparison;
   decode        the decode step (ssd_step) at the same layer shape, batch 1 and 8;
   stack         the 24-layer vertical stack (segmented entry point, wavefront and one
                 step at a time, and the horizontal order), a secondary figure;
@@ -50,6 +52,8 @@ def parse():
                     help="skip the secondary timing of the 24-layer vertical stack")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary timing of the decode step")
+    ap.add_argument("--no-scan-form", action="store_true",
+                    help="skip the secondary timing of the associative-scan form of the chunk outputs")
     ap.add_argument("--kernel-steps", type=int, default=0, help="launches per kernel for per-kernel timing "
                     "(default: --steps)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -317,6 +321,24 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+    if not args.no_scan_form:
+        print("[bench] scan form", file=sys.stderr, flush=True)
+        sf = {"workload": w.name, "stage": "chunk outputs (stage 4)"}
+        for name, scan_form in (("matrix_core", False), ("scan_form", True)):
+            step()
+            torch.cuda.synchronize()
+            reps = 3 if scan_form else 10
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                ssd.fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["init_state"], w.chunk, y=y,
+                        final_state=fin, workspace=ws, stream=stream, first_stage=ssd.NSTAGES,
+                        last_stage=ssd.NSTAGES, scan_form=scan_form)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            sf["us_" + name] = round(e0.elapsed_time(e1) / reps * 1e3, 1)
+        sf["ratio"] = round(sf["us_scan_form"] / sf["us_matrix_core"], 1)
+        out["scan_form"] = sf
     if not args.no_decode:
         print("[bench] decode step", file=sys.stderr, flush=True)
         out["decode"] = decode_timing(torch, dev)

@@ -9,9 +9,11 @@
 // One workgroup per (batch, chunk, head), one wave per window of 64 tokens, lane = token.
 // For each state element (p, n):
 //   - every lane forms v_t = x_t[p] B_t[n] and the wave runs an inclusive tree scan over
-//     its 64 tokens in log2(64) = 6 shuffle steps (span 1, 2, 4, ..., 32), the step of span
-//     d multiplying the partner's value by the decay exp(cum_t - cum_{t-d}) (per lane,
-//     computed once from the chunk's dA_cum row);
+//     its 64 tokens in log2(64) = 6 cross-lane steps: spans 1, 2, 4, 8 inside each
+//     16-lane row (DPP row shifts), then the end of row r joined to row r + 1 and lane 31
+//     to rows 2-3 (DPP row broadcasts); every step multiplies the incoming partial value
+//     by the decay across the span it skips, exp(cum_t - cum_s) (per lane, computed once
+//     from the chunk's dA_cum row);
 //   - lane 63 leaves its window's end value in LDS; the state entering window w is then
 //     exp(cum_{64w-1}) b_in + sum_{w' < w} exp(cum_{64w-1} - cum_{64w'+63}) end_{w'}
 //     (the top levels of the tree, across the chunk's Q/64 windows), and reaches token t
@@ -19,12 +21,12 @@
 //   - y_t[p] accumulates C_t[n] h_t[n] over n in a register.
 // y_t = sum_n C_t[n] h_t[n] + (D + residual) x_t, rounded once to the activation dtype.
 // B and C of the chunk are staged once in LDS with one padding word per row, so the 64
-// lanes (64 different rows) read different banks.
+// lanes (64 different rows) read different banks; b(c-1) is staged row-major.
 #include "ssd_common.h"
 
 namespace ssd {
 
-template <typename T, int Q, int N>
+template <typename T, int Q, int P, int N>
 struct AssocCfg {
     static constexpr int NWIN = Q >= 64 ? Q / 64 : 1;           // waves (64-token windows)
     static constexpr int THREADS = NWIN * 64;
@@ -32,9 +34,19 @@ struct AssocCfg {
     static constexpr int WPR = N / EPW;                         // words per row
     static constexpr int RSW = WPR + 1;                         // LDS row stride in words
     static constexpr int TILE_BYTES = Q * RSW * 4;              // one of B, C
-    static constexpr int LDS = 2 * TILE_BYTES + 2 * NWIN * N * 4;
+    static constexpr int END_BYTES = 2 * NWIN * N * 4;          // window end values, double-buffered
+    static constexpr int BIN_BYTES = P * N * (int)sizeof(T);    // b(c-1), row-major
+    static constexpr int LDS = 2 * TILE_BYTES + END_BYTES + BIN_BYTES;
     static constexpr bool OK = LDS <= kLdsBytes;
 };
+
+// One step of the in-wave tree: the value of the lane selected by the DPP control (0
+// where there is none), times this lane's decay across the skipped span, added.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float tree_step(float v, float m) {
+    const int u = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xf, true);
+    return fmaf(m, __builtin_bit_cast(float, u), v);
+}
 
 // Element e (0 .. EPW-1) of an LDS word.
 template <typename T>
@@ -46,14 +58,9 @@ __device__ __forceinline__ float word_elem<bf16>(uint32_t wd, int e) {
     return __uint_as_float(e ? (wd & 0xffff0000u) : (wd << 16));
 }
 
-// Element (p, n) of one P x N state stored in tile order (see libssdscan.h).
-__device__ __forceinline__ int64_t tile_index(int p, int n, int PT) {
-    return ((int64_t)((n >> 4) * PT + (p >> 4)) * 64 + ((p & 15) + 16 * ((n & 15) >> 2))) * 4 + (n & 3);
-}
-
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__((AssocCfg<T, Q, N>::THREADS)) void chunk_scan_assoc_kernel(Problem p0) {
-    using Cfg = AssocCfg<T, Q, N>;
+__global__ __launch_bounds__((AssocCfg<T, Q, P, N>::THREADS)) void chunk_scan_assoc_kernel(Problem p0) {
+    using Cfg = AssocCfg<T, Q, P, N>;
     typedef typename CumT<T>::type S;
     constexpr int NWIN = Cfg::NWIN, EPW = Cfg::EPW, WPR = Cfg::WPR, RSW = Cfg::RSW;
     constexpr int PT = P / 16;
@@ -61,6 +68,7 @@ __global__ __launch_bounds__((AssocCfg<T, Q, N>::THREADS)) void chunk_scan_assoc
     uint32_t *Bs = reinterpret_cast<uint32_t *>(smem);
     uint32_t *Cs = Bs + Q * RSW;
     float *endv = reinterpret_cast<float *>(Cs + Q * RSW);    // [2][NWIN][N]
+    uint32_t *bins = reinterpret_cast<uint32_t *>(endv + 2 * NWIN * N);   // b(c-1) [P][N] as words
 
     const Problem p = step_problem(p0, blockIdx.y);
     const int logical = blockIdx.x;                            // (b, c, h)
@@ -102,13 +110,18 @@ __global__ __launch_bounds__((AssocCfg<T, Q, N>::THREADS)) void chunk_scan_assoc
     const S ct = cum[tc];
     const S cws = w > 0 ? cum[w * 64 - 1] : (S)0;             // sum before this window
     const float Pw = __expf((float)(ct - cws));                // window start .. t
-    float M[6];                                                // tree step of span 2^s
+    // decays of the six tree steps: row shifts by d = 1, 2, 4, 8 (from lane t - d of the
+    // same 16-lane row), then row ends (rows 1 and 3 take the end of the row before) and
+    // lane 31 (rows 2 and 3); zero where the step adds nothing or the lane is past Q
+    const int lr = lane & 15, row = lane >> 4, w0 = w * 64;
+    float M[6];
 #pragma unroll
-    for (int s = 0; s < 6; ++s) {
+    for (int s = 0; s < 4; ++s) {
         const int d = 1 << s;
-        // lane >= d and t < Q keep t - d inside the chunk's row
-        M[s] = (lane >= d && t < Q) ? __expf((float)(ct - cum[t - d >= 0 ? t - d : 0])) : 0.f;
+        M[s] = (lr >= d && t < Q) ? __expf((float)(ct - cum[t - d >= 0 ? t - d : 0])) : 0.f;
     }
+    M[4] = ((row & 1) && t < Q) ? __expf((float)(ct - cum[min(w0 + 16 * row - 1, Q - 1)])) : 0.f;
+    M[5] = (row >= 2 && t < Q) ? __expf((float)(ct - cum[w0 + 31])) : 0.f;
     const float Dwin = __expf((float)cws);                     // chunk start .. window start
     float Dww[NWIN];                                           // end of window w' .. window start
 #pragma unroll
@@ -116,39 +129,70 @@ __global__ __launch_bounds__((AssocCfg<T, Q, N>::THREADS)) void chunk_scan_assoc
     const float dres = (p.D ? p.D[h] : 0.f) + ((p.flags & 1u) ? 1.f : 0.f);
     const T *xr = reinterpret_cast<const T *>(p.x) + (int64_t)b * p.x_bs + (int64_t)(t0 + (act ? t : 0)) * HP + h * P;
     T *yr = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)(t0 + (act ? t : 0)) * HP + h * P;
-    const T *bin = reinterpret_cast<const T *>(p.b_in) + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)P * N;
+    // b(c-1) (tile order in the workspace) -> LDS, row-major [P][N]: 4 consecutive n per piece
+    {
+        const T *bin = reinterpret_cast<const T *>(p.b_in) + (((int64_t)b * p.nc + c) * p.H + h) * (int64_t)P * N;
+        T *bl = reinterpret_cast<T *>(bins);
+        for (int e4 = tid; e4 < P * N / 4; e4 += Cfg::THREADS) {
+            const int e = e4 * 4, tile = e >> 8, l = (e >> 2) & 63;
+            const int pr = (tile % PT) * 16 + (l & 15), n0 = (tile / PT) * 16 + 4 * (l >> 4);
+            typedef typename TF<T>::type F;
+            *reinterpret_cast<F *>(bl + pr * N + n0) = *reinterpret_cast<const F *>(bin + e);
+        }
+    }
     __syncthreads();
 
     for (int pp = 0, par = 0; pp < P; ++pp, par ^= 1) {
         const float xv = act ? to_f32(xr[pp]) : 0.f;
         float yl = 0.f;
         float *ev = endv + (par * NWIN + w) * N;
-        for (int k = 0; k < WPR; ++k) {
-            const uint32_t bw = Bs[t < Q ? t * RSW + k : k];
-            const uint32_t cw = Cs[t < Q ? t * RSW + k : k];
+        // elements in groups of 64: lane 63's end value of element n is selected into lane
+        // n % 64 of endacc (no per-element branch), then one LDS write per group
+        constexpr int NH = (N + 63) / 64, WPH = 64 / EPW;
 #pragma unroll
-            for (int e = 0; e < EPW; ++e) {
-                float v = t < Q ? xv * word_elem<T>(bw, e) : 0.f;
+        for (int hh = 0; hh < NH; ++hh) {
+            int endacc = 0;
+            // several words per iteration: their scans are independent chains, which hides
+            // the latency of the cross-lane steps (one wave per SIMD at this LDS size)
+#pragma unroll 8
+            for (int k = hh * WPH; k < (WPR < (hh + 1) * WPH ? WPR : (hh + 1) * WPH); ++k) {
+                const uint32_t bw = Bs[t < Q ? t * RSW + k : k];
+                const uint32_t cw = Cs[t < Q ? t * RSW + k : k];
 #pragma unroll
-                for (int s = 0; s < 6; ++s) {                 // inclusive tree scan over the window
-                    const float u = __shfl_up(v, 1 << s, 64);
-                    if (lane >= (1 << s)) v = fmaf(M[s], u, v);
+                for (int e = 0; e < EPW; ++e) {
+                    float v = t < Q ? xv * word_elem<T>(bw, e) : 0.f;
+                    // inclusive tree scan over the window (DPP: row_shr 1, 2, 4, 8; row_bcast
+                    // 15 into rows 1 and 3; row_bcast 31 into rows 2 and 3)
+                    v = tree_step<0x111, 0xf>(v, M[0]);
+                    v = tree_step<0x112, 0xf>(v, M[1]);
+                    v = tree_step<0x114, 0xf>(v, M[2]);
+                    v = tree_step<0x118, 0xf>(v, M[3]);
+                    v = tree_step<0x142, 0xa>(v, M[4]);
+                    v = tree_step<0x143, 0xc>(v, M[5]);
+                    yl = fmaf(word_elem<T>(cw, e), v, yl);
+                    const int last = __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63);
+                    endacc = lane == k * EPW + e - hh * 64 ? last : endacc;
                 }
-                yl = fmaf(word_elem<T>(cw, e), v, yl);
-                if (lane == 63) ev[k * EPW + e] = v;
             }
+            if (hh * 64 + lane < N) ev[hh * 64 + lane] = __builtin_bit_cast(float, endacc);
         }
         __syncthreads();                                        // every window's end values
         // state entering this window, contracted with C_t
         float yc = 0.f;
         const float *e0 = endv + par * NWIN * N;
-        for (int n = 0; n < N; ++n) {
-            float K = Dwin * to_f32(bin[tile_index(pp, n, PT)]);
+#pragma unroll 8
+        for (int k = 0; k < WPR; ++k) {
+            const uint32_t bw = bins[pp * WPR + k];            // same word for every lane
+            const uint32_t cw = Cs[(t < Q ? t : 0) * RSW + k];
 #pragma unroll
-            for (int v = 0; v < NWIN; ++v)
-                if (v < w) K = fmaf(Dww[v], e0[v * N + n], K);
-            const uint32_t cw = Cs[(t < Q ? t : 0) * RSW + n / EPW];
-            yc = fmaf(word_elem<T>(cw, n % EPW), K, yc);
+            for (int e = 0; e < EPW; ++e) {
+                const int n = k * EPW + e;
+                float K = Dwin * word_elem<T>(bw, e);
+#pragma unroll
+                for (int v = 0; v < NWIN; ++v)
+                    if (v < w) K = fmaf(Dww[v], e0[v * N + n], K);
+                yc = fmaf(word_elem<T>(cw, e), K, yc);
+            }
         }
         if (act) yr[pp] = from_f32<T>(fmaf(Pw, yc, yl) + dres * xv);
     }
@@ -156,7 +200,7 @@ __global__ __launch_bounds__((AssocCfg<T, Q, N>::THREADS)) void chunk_scan_assoc
 
 template <typename T, int Q, int P, int N>
 static hipError_t launch_assoc_t(const Problem &p, hipStream_t s) {
-    using Cfg = AssocCfg<T, Q, N>;
+    using Cfg = AssocCfg<T, Q, P, N>;
     if constexpr (!Cfg::OK) {
         return hipErrorInvalidValue;
     } else {
@@ -175,7 +219,7 @@ static hipError_t launch_assoc_t(const Problem &p, hipStream_t s) {
 #define SSD_ASSOC_CASE(T, q, pp, nn) \
     if (p.Q == q && p.P == pp && p.N == nn) return launch_assoc_t<T, q, pp, nn>(p, s);
 #define SSD_ASSOC_OK(T, q, pp, nn) \
-    if (Q == q && P == pp && N == nn) return AssocCfg<T, q, nn>::OK;
+    if (Q == q && P == pp && N == nn) return AssocCfg<T, q, pp, nn>::OK;
 
 hipError_t launch_chunk_scan_assoc(const Problem &p, hipStream_t s) {
     if (p.dtype == 1) { SSD_ASSOC_SHAPES(SSD_ASSOC_CASE, bf16) }
