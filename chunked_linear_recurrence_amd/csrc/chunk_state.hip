@@ -45,14 +45,14 @@ template <> struct Row16T<bf16> { typedef bf16x8 type; };
 template <> struct Row16T<float> { typedef f32x4 type; };
 
 // Loads rows [j0, j0 + RJ) x cols [c0, c0 + 16 bytes) of a token-major tile (row pitch
-// `pitch` elements), zero past `rows`.
+// `pitch` elements), zero past `rows`.  Non-temporal: x and B are streamed once here.
 template <typename T, int RJ>
 __device__ __forceinline__ void load_block(const T *base, int64_t pitch, int j0, int c0, int rows,
                                            typename Row16T<T>::type (&r)[RJ]) {
     typedef typename Row16T<T>::type V;
 #pragma unroll
     for (int i = 0; i < RJ; ++i) {
-        if (j0 + i < rows) r[i] = *reinterpret_cast<const V *>(base + (int64_t)(j0 + i) * pitch + c0);
+        if (j0 + i < rows) r[i] = __builtin_nontemporal_load(reinterpret_cast<const V *>(base + (int64_t)(j0 + i) * pitch + c0));
         else r[i] = V{};
     }
 }
@@ -210,7 +210,8 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_k
             const int nt = wave * Cfg::NTW + i;
 #pragma unroll
             for (int pt = 0; pt < Cfg::PT; ++pt)
-                *reinterpret_cast<F *>(out + ((nt * Cfg::PT + pt) * 64 + lane) * 4) = frag_from_f32<T>(acc[i][pt]);
+                __builtin_nontemporal_store(frag_from_f32<T>(acc[i][pt]),   // written once, read by state_pass
+                                            reinterpret_cast<F *>(out + ((nt * Cfg::PT + pt) * 64 + lane) * 4));
         }
     }
 }

@@ -13,7 +13,9 @@
 // batch * H * P * N / 256 independent waves.  The loads of b_intra do not depend on the
 // carried state, so they run two groups of K chunks ahead of the dependent multiply-adds
 // (K loads of the next group are in flight while the current group is consumed); the pass
-// is a pure HBM stream (read and write act bytes per state element per chunk).
+// is a pure HBM stream (read and write act bytes per state element per chunk); b_intra is
+// read with the non-temporal policy (used once), b_in is stored normally (chunk_scan reads
+// it next, and keeping its stores cacheable measured faster than streaming them).
 //
 // b_intra and b_in use the tile order of the other kernels (see libssdscan.h); only
 // init_state / final_state use the row-major [P][N] order, so the thread owning tile
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(64) void state_pass_kernel(Problem p0) {
 #pragma unroll
         for (int u = 0; u < K; ++u)
             if (c0 + u < nc) {                               // uniform
-                v[u] = *reinterpret_cast<const V *>(bi + (int64_t)(c0 + u) * cstride);
+                v[u] = __builtin_nontemporal_load(reinterpret_cast<const V *>(bi + (int64_t)(c0 + u) * cstride));
                 d[u] = cum[(int64_t)(c0 + u) * p.Q];
             }
     };
