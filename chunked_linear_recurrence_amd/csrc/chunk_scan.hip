@@ -33,7 +33,7 @@
 //       upper triangle of S^T does the masking); a lane's 4 S^T values are 4 consecutive
 //       k values of the B operand, so no data moves between lanes;
 //     y^T += x^T diag(D + residual) on the matrix cores (D split in a high and a low bf16
-//       part so the skip term keeps fp32 accuracy).
+//       part so the skip term keeps fp32 accuracy; K = 16 products).
 // Tiles are paired into 16x16x32 bf16 products (16x16x4 f32 for the fp32 dtype).
 #include "ssd_common.h"
 
@@ -256,20 +256,22 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
     // and a low part in the operand dtype, A operand the x fragments of the diagonal block.
     {
         F dhi, dlo;
+        const float hi = to_f32(from_f32<T>(dres)), lo = dres - hi;   // uniform
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float v = (g4 + e == col) ? dres : 0.f;
-            dhi[e] = from_f32<T>(v);
-            dlo[e] = from_f32<T>(v - to_f32(dhi[e]));
+            dhi[e] = from_f32<T>((g4 + e == col) ? hi : 0.f);
+            dlo[e] = from_f32<T>((g4 + e == col) ? lo : 0.f);
         }
 #pragma unroll
         for (int ri = 0; ri < 2; ++ri) {
             const int I = ri ? I1 : I0;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
+                // K = 16 products: x's fragment is the A operand as it is (a K = 32 product
+                // would need it twice in consecutive registers)
                 const F xv = x_frag<T, P>(xs, I, pt, lane);
-                if constexpr (sizeof(T) == 2) acc[ri][pt] = mma_pair(xv, dhi, xv, dlo, acc[ri][pt]);
-                else acc[ri][pt] = mma_one(xv, dhi, acc[ri][pt]);
+                acc[ri][pt] = mma_one(xv, dhi, acc[ri][pt]);
+                if constexpr (sizeof(T) == 2) acc[ri][pt] = mma_one(xv, dlo, acc[ri][pt]);
             }
         }
     }
@@ -351,10 +353,11 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
             // row or writes past its LDS region
             const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
             const int pc = w * 64 + lane;
-            if (pc < CP)
+            // a per-wave test where the pieces fill whole waves (no exec-mask branch)
+            if ((CP % 64 == 0) ? (w * 64 < CP) : (pc < CP))
                 dma16(reinterpret_cast<const unsigned char *>(reinterpret_cast<const S *>(p.dA_cum) + tok) + pc * 16,
                       buf + Buf::O_CM + w * 1024);
-            if (pc < FP) {
+            if ((FP % 64 == 0) ? (w * 64 < FP) : (pc < FP)) {
                 dma16(reinterpret_cast<const unsigned char *>(p.decF + tok) + pc * 16, buf + Buf::O_F + w * 1024);
                 dma16(reinterpret_cast<const unsigned char *>(p.decG + tok) + pc * 16, buf + Buf::O_G + w * 1024);
             }
@@ -375,9 +378,11 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         const int i = (row < 16 ? I0 : I1) * 16 + (row & 15);
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + (row * YPIECES + (q ^ ysw<YPIECES>(row))) * 16);
-        if (i < Qc)   // y is written once and not read again in this step: non-temporal
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(ychunk + (int64_t)i * HP + (int64_t)hs * P +
-                                                                     q * (16 / (int)sizeof(T))));
+        // y is written once and not read again in this step: non-temporal.  Only the last
+        // chunk can be short, so full chunks skip the per-lane row check.
+        u32x4 *dst = reinterpret_cast<u32x4 *>(ychunk + (int64_t)i * HP + (int64_t)hs * P + q * (16 / (int)sizeof(T)));
+        if (Qc == Q) __builtin_nontemporal_store(v, dst);
+        else if (i < Qc) __builtin_nontemporal_store(v, dst);
     };
 
 #pragma unroll
