@@ -207,18 +207,6 @@ __device__ __forceinline__ typename TF<T>::type frag_from_f32(f32x4 v) {
     return r;
 }
 
-template <typename T>
-__device__ __forceinline__ f32x4 frag_to_f32(typename TF<T>::type v) {
-    f32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = to_f32(v[i]);
-    return r;
-}
-
-// 16-byte row piece of an activation tile, as raw 32-bit words.
-struct Row16 { uint32_t w[4]; };
-struct Row8 { uint32_t w[2]; };
-
 // Consecutive workgroups go round-robin to the 8 XCDs (each with its own L2).  Remap so
 // that logically adjacent workgroups (which share B/C data) land on the same XCD.
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
