@@ -74,14 +74,13 @@ def alg_bytes(w):
     dt = b * L * H * e
     bc = b * L * G * N * e                      # one of B or C
     cum = b * H * nc * Q * cum_e                # dA_cum
-    fg = 2 * b * H * nc * Q * 4                 # the two float32 decay factors per token-head
     states = b * nc * H * P * N
     init = final = b * H * P * N * 4
     k = {
-        "chunk_cumsum": dt + cum + fg,
+        "chunk_cumsum": dt + cum,
         "chunk_state": x + bc + cum + states * e,
         "state_pass": 2 * states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
-        "chunk_scan": x + 2 * bc + cum + fg + states * e + y,
+        "chunk_scan": x + 2 * bc + cum + states * e + y,
     }
     method = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final + 4 * states * e
     return k, method

@@ -6,10 +6,6 @@
 //
 // Layout: dA_cum[b, h, c, i], i < Q.  Positions past a short last chunk hold the chunk
 // total, so later kernels can read any index without special cases.
-// Two float32 decay factors per token go to the same layout for chunk_scan:
-//   decF[i] = exp(cum[end(i)] - cum[i])   with end(i) the last token of i's 16-token block,
-//   decG[i] = exp(cum[i]);
-// both lie in [0, 1] when A <= 0.
 // Sums are float64 for float32 activations (dt * A is then exact) and float32 for
 // bfloat16 activations.
 //
@@ -99,20 +95,6 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
 #pragma unroll
         for (int e = 0; e < E; ++e) cv[e] = (lane * E + e <= last) ? excl + v[e] : lastv;
         if (active) store_run<S, E>(out, cv);
-        // block end of this lane's tokens (E divides 16, so they share one block)
-        const int src = ((lane * E) / 16 * 16 + 15) / E;
-        const S cend = __shfl(cv[E - 1], src, 64);
-        const int64_t fo = (((int64_t)b * p.H + hb + hh) * p.nc + c) * Q + lane * E;
-        float fv[E], gv[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            fv[e] = expf((float)(cend - cv[e]));
-            gv[e] = expf((float)cv[e]);
-        }
-        if (active) {
-            store_run<float, E>(p.decF + fo, fv);
-            store_run<float, E>(p.decG + fo, gv);
-        }
     }
 }
 

@@ -22,16 +22,15 @@
 // formed once per chunk and group, never per head.
 //
 // Per head, x is brought into LDS by DMA (tokens x channels, read back as transposed
-// fragments), b_in likewise, and three per-token factors: cum_j, F_j =
-// exp(cum_end(j) - cum_j), G_j = exp(cum_j), where end(j) is the last token of j's
-// 16-token block.  The products are computed transposed (y^T[p][i]) so that a lane's 4
-// accumulator values are 4 consecutive channels of one token:
-//     Z^T = b(c-1) C^T, column i scaled by G_i;
-//     y^T += x^T (S^T . decay), where an off-diagonal tile (J < I) factorises the decay as
-//       exp(cum_i - cum_j) = exp(cum_i - cum_end(J)) * F_j (both factors <= 1, one exp per
-//       lane and tile) and the diagonal tile uses exp(min(cum_i - cum_j, 0)) (the zeroed
-//       upper triangle of S^T does the masking); a lane's 4 S^T values are 4 consecutive
-//       k values of the B operand, so no data moves between lanes;
+// fragments), b_in likewise, and the chunk's log-decay prefix sums cum.  The products are
+// computed transposed (y^T[p][i]) so that a lane's 4 accumulator values are 4 consecutive
+// channels of one token:
+//     Z^T = b(c-1) C^T, column i scaled by G_i = exp(cum_i);
+//     y^T += x^T (S^T . decay), the decay of tile entry (j, i) being exp(cum_i - cum_j):
+//       <= 1 below the diagonal (cum is non-increasing), and exp(min(cum_i - cum_j, 0)) on
+//       diagonal tiles (the zeroed upper triangle of S^T does the masking); a lane's 4 S^T
+//       values are 4 consecutive k values of the B operand, so no data moves between
+//       lanes;
 //     y^T += x^T diag(D + residual) on the matrix cores (D split in a high and a low bf16
 //       part so the skip term keeps fp32 accuracy; K = 16 products).
 // Tiles are paired into 16x16x32 bf16 products (16x16x4 f32 for the fp32 dtype).
@@ -147,9 +146,8 @@ struct HeadBuf {
     static constexpr int X = Q * P * (int)sizeof(T);
     static constexpr int ST = P * N * (int)sizeof(T);
     static constexpr int CM = Q * (int)sizeof(S);
-    static constexpr int FG = Q * 4;
-    static constexpr int O_ST = X, O_CM = X + ST, O_F = X + ST + CM, O_G = O_F + FG;
-    static constexpr int BYTES = O_G + FG;
+    static constexpr int O_ST = X, O_CM = X + ST;
+    static constexpr int BYTES = O_CM + CM;
 };
 
 // Per-head products of wave W (all slot choices and offsets are compile-time):
@@ -177,8 +175,6 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
     const unsigned char *xs = buf;
     const T *stb = reinterpret_cast<const T *>(buf + Buf::O_ST);
     const S *cm = reinterpret_cast<const S *>(buf + Buf::O_CM);
-    const float *Fv = reinterpret_cast<const float *>(buf + Buf::O_F);
-    const float *Gv = reinterpret_cast<const float *>(buf + Buf::O_G);
 
     // Output tiles are transposed: acc[ri][pt] lane (col, g), value r holds
     // y^T[p = pt*16 + 4g + r][i = I*16 + col].
@@ -207,7 +203,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
     }
     const S ci0 = cm[I0 * 16 + col], ci1 = cm[I1 * 16 + col];
     {
-        const float gi0 = Gv[I0 * 16 + col], gi1 = Gv[I1 * 16 + col];
+        const float gi0 = __expf((float)ci0), gi1 = __expf((float)ci1);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -230,10 +226,9 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
             Jx[u] = sl.J;
             f32x4 m;
             if (sl.J < sl.I) {                              // uniform: off-diagonal tile or pad
-                const float e = __expf((float)(ci - cm[sl.J * 16 + 15]));
-                const f32x4 fj = *reinterpret_cast<const f32x4 *>(Fv + sl.J * 16 + g4);
+                // cum is non-increasing (dt A <= 0), so ci - cum_j <= 0 here
 #pragma unroll
-                for (int r = 0; r < 4; ++r) m[r] = sT[s][r] * (e * fj[r]);
+                for (int r = 0; r < 4; ++r) m[r] = sT[s][r] * __expf((float)(ci - cm[sl.J * 16 + g4 + r]));
             } else {                                        // diagonal (masked in S^T)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -297,7 +292,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     // memory work per head and wave, in single-instruction items:
     constexpr int XK = (Q * XPIECES + THREADS - 1) / THREADS;           // x tile
     constexpr int SP = Buf::ST / 16, SK = (SP + THREADS - 1) / THREADS;  // b_in state
-    constexpr int CP = Buf::CM / 16, FP = Buf::FG / 16;                  // cum, F, G
+    constexpr int CP = Buf::CM / 16;                                     // cum
     constexpr int NDMA = XK + SK + 1;
     constexpr int NSTQ = 32 * YPIECES / 64;                               // staged-output stores
     constexpr int NHOOK = 1 + PT + Cfg::NPAIR;
@@ -348,22 +343,18 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
                 dma16(sv + ((kk * NW + w) * 64 + lane) * 16, buf + Buf::O_ST + (kk * NW + w) * 1024);
             }
         } else {
-            // cum, F and G of one (head, chunk) are CP and FP 16-byte pieces, which need not
-            // fill whole waves (Q < 256): the guard is per lane, so no lane reads past the
-            // row or writes past its LDS region
+            // cum of one (head, chunk) is CP 16-byte pieces, which need not fill whole
+            // waves (Q < 256 for bf16): the guard is per lane, so no lane reads past the row
+            // or writes past its LDS region
             const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
             const int pc = w * 64 + lane;
             // a per-wave test where the pieces fill whole waves (no exec-mask branch)
             if ((CP % 64 == 0) ? (w * 64 < CP) : (pc < CP))
                 dma16(reinterpret_cast<const unsigned char *>(reinterpret_cast<const S *>(p.dA_cum) + tok) + pc * 16,
                       buf + Buf::O_CM + w * 1024);
-            if ((FP % 64 == 0) ? (w * 64 < FP) : (pc < FP)) {
-                dma16(reinterpret_cast<const unsigned char *>(p.decF + tok) + pc * 16, buf + Buf::O_F + w * 1024);
-                dma16(reinterpret_cast<const unsigned char *>(p.decG + tok) + pc * 16, buf + Buf::O_G + w * 1024);
-            }
         }
     };
-    static_assert(CP <= THREADS && FP <= THREADS, "cum/F/G fit one DMA item");
+    static_assert(CP <= THREADS, "cum fits one DMA item");
     // the x, state and B pieces always fill whole waves, so their guards are uniform
     static_assert((Q * XPIECES) % 64 == 0 && SP % 64 == 0 && (Q * Cfg::BPIECES) % 64 == 0,
                   "x, state and B tiles are whole waves of 16-byte pieces");

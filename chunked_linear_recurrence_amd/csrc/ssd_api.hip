@@ -41,7 +41,7 @@ constexpr int kStages = 4;   // chunk_cumsum, chunk_state, state_pass, chunk_sca
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t dA, bintra, bin, decF, decG, total;
+    size_t dA, bintra, bin, total;
 };
 
 int64_t act_bytes(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
@@ -68,10 +68,6 @@ bool layout_for(const ssd_dims_t &d, int64_t L, int32_t Q, Layout *lo) {
     off += align_up((size_t)states * act_bytes(d.dtype));
     lo->bin = off;
     off += align_up((size_t)states * act_bytes(d.dtype));
-    lo->decF = off;
-    off += align_up((size_t)t * 4);
-    lo->decG = off;
-    off += align_up((size_t)t * 4);
     lo->total = off;
     return true;
 }
@@ -220,8 +216,6 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     p.dA_cum = ws + lo.dA;
     p.b_intra = ws + lo.bintra;
     p.b_in = ws + lo.bin;
-    p.decF = reinterpret_cast<float *>(ws + lo.decF);
-    p.decG = reinterpret_cast<float *>(ws + lo.decG);
     st = run_layer(p, static_cast<hipStream_t>(stream), first_stage, last_stage);
     return st == SSD_OK ? ok() : st;
 }
@@ -375,8 +369,6 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
         q.o_dA = sl.lo.dA;
         q.o_bintra = sl.lo.bintra;
         q.o_bin = sl.lo.bin;
-        q.o_decF = sl.lo.decF;
-        q.o_decG = sl.lo.decG;
         q.dt0 = dt;
         q.B0 = B;
         q.C0 = C;
@@ -424,8 +416,6 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
                 p.dA_cum = lws + sl.lo.dA;
                 p.b_intra = lws + sl.lo.bintra;
                 p.b_in = lws + sl.lo.bin;
-                p.decF = reinterpret_cast<float *>(lws + sl.lo.decF);
-                p.decG = reinterpret_cast<float *>(lws + sl.lo.decG);
                 st = run_layer(p, s, 1, kStages);
                 if (st != SSD_OK) return st;
             }

@@ -18,16 +18,14 @@ def layout(e, Q, P, N):
     cum_e = 8 if e == 4 else 4
     NRB = Q // 16
     NW = NRB // 2
-    X, ST, CM, FG = Q * P * e, P * N * e, Q * cum_e, Q * 4
+    X, ST, CM = Q * P * e, P * N * e, Q * cum_e
     O_ST, O_CM = X, X + ST
-    O_F = O_CM + CM
-    O_G = O_F + FG
-    BYTES = O_G + FG
+    BYTES = O_CM + CM
     DB = 2 * BYTES <= LDS_MAX
     YP, YW = P * e // 16, 32 * P * e
     YS = DB and 2 * BYTES + NW * YW <= LDS_MAX
     LDS = (2 * BYTES if DB else BYTES) + (NW * YW if YS else 0)
-    return dict(NW=NW, THREADS=NW * 64, X=X, ST=ST, CM=CM, FG=FG, O_ST=O_ST, O_CM=O_CM, O_F=O_F, O_G=O_G,
+    return dict(NW=NW, THREADS=NW * 64, X=X, ST=ST, CM=CM, O_ST=O_ST, O_CM=O_CM,
                 BYTES=BYTES, DB=DB, YP=YP, YW=YW, YS=YS, LDS=LDS, XP=P * e // 16, BP=N * e // 16,
                 BL=DB and Q * N * e <= LDS - BYTES)
 
@@ -47,9 +45,9 @@ def cases():
 def test_chunk_scan_dma_and_staging_in_bounds(e, Q, P, N):
     c = layout(e, Q, P, N)
     NW, THREADS, XP, BP = c["NW"], c["THREADS"], c["XP"], c["BP"]
-    SP, CP, FP = c["ST"] // 16, c["CM"] // 16, c["FG"] // 16
+    SP, CP = c["ST"] // 16, c["CM"] // 16
     XK, SK = -(-Q * XP // THREADS), -(-SP // THREADS)
-    assert CP <= THREADS and FP <= THREADS
+    assert CP <= THREADS
     assert (Q * XP) % 64 == 0 and SP % 64 == 0 and (Q * BP) % 64 == 0   # whole-wave tiles
 
     def swz(r):
@@ -67,13 +65,9 @@ def test_chunk_scan_dma_and_staging_in_bounds(e, Q, P, N):
                 pc = (k * NW + w) * 64 + lane
                 assert pc * 16 + 16 <= c["ST"]
                 assert c["O_ST"] + (k * NW + w) * 1024 + lane * 16 + 16 <= c["O_CM"]
-        pc = w * 64 + lane                                      # cum, F, G: per-lane guard
+        pc = w * 64 + lane                                      # cum: per-lane guard
         if pc < CP:
-            assert pc * 16 + 16 <= c["CM"] and c["O_CM"] + w * 1024 + lane * 16 + 16 <= c["O_F"]
-        if pc < FP:
-            assert pc * 16 + 16 <= c["FG"]
-            assert c["O_F"] + w * 1024 + lane * 16 + 16 <= c["O_G"]
-            assert c["O_G"] + w * 1024 + lane * 16 + 16 <= c["BYTES"]
+            assert pc * 16 + 16 <= c["CM"] and c["O_CM"] + w * 1024 + lane * 16 + 16 <= c["BYTES"]
         if c["BL"]:                                             # B tile beside the first buffer
             for k in range(-(-Q * BP // THREADS)):
                 if (k * NW + w) * 64 < Q * BP:
@@ -88,9 +82,9 @@ def test_chunk_scan_dma_and_staging_in_bounds(e, Q, P, N):
 
 def test_a_per_wave_guard_on_short_decay_rows_would_overrun():
     """The model detects the bug class: with Q = 64 a decay row is 16 pieces, so letting all
-    64 lanes of wave 0 copy overruns the 256-byte region."""
+    64 lanes of wave 0 copy overruns the 256-byte region (past the end of the head buffer)."""
     c = layout(2, 64, 64, 128)
     CP = c["CM"] // 16
     assert CP < 64
     lanes = range(64)                                           # what a per-wave guard admits
-    assert any(c["O_CM"] + lane * 16 + 16 > c["O_F"] for lane in lanes)
+    assert any(c["O_CM"] + lane * 16 + 16 > c["BYTES"] for lane in lanes)
