@@ -5,7 +5,8 @@
 // intra-chunk decay.
 //
 // Layout: dA_cum[b, h, c, i], i < Q.  Positions past a short last chunk hold the chunk
-// total, so later kernels can read any index without special cases.
+// total, so later kernels can read any index without special cases.  The totals are also
+// written contiguously, ctot[b, h, c], for the state pass.
 // Sums are float64 for float32 activations (dt * A is then exact) and float32 for
 // bfloat16 activations.
 //
@@ -95,6 +96,8 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
 #pragma unroll
         for (int e = 0; e < E; ++e) cv[e] = (lane * E + e <= last) ? excl + v[e] : lastv;
         if (active) store_run<S, E>(out, cv);
+        if (lane == 0)                               // the chunk's total, for the state pass
+            reinterpret_cast<S *>(p.ctot)[((int64_t)b * p.H + hb + hh) * p.nc + c] = lastv;
     }
 }
 

@@ -41,7 +41,7 @@ constexpr int kStages = 4;   // chunk_cumsum, chunk_state, state_pass, chunk_sca
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t dA, bintra, bin, total;
+    size_t dA, bintra, bin, ctot, total;
 };
 
 int64_t act_bytes(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
@@ -68,6 +68,9 @@ bool layout_for(const ssd_dims_t &d, int64_t L, int32_t Q, Layout *lo) {
     off += align_up((size_t)states * act_bytes(d.dtype));
     lo->bin = off;
     off += align_up((size_t)states * act_bytes(d.dtype));
+    // each chunk's total log-decay, contiguous per (batch, head) for the state pass
+    lo->ctot = off;
+    off += align_up((size_t)bhn * (d.dtype == SSD_F32 ? 8 : 4));
     lo->total = off;
     return true;
 }
@@ -214,6 +217,7 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     p.flags = flags;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     p.dA_cum = ws + lo.dA;
+    p.ctot = ws + lo.ctot;
     p.b_intra = ws + lo.bintra;
     p.b_in = ws + lo.bin;
     st = run_layer(p, static_cast<hipStream_t>(stream), first_stage, last_stage);
@@ -367,6 +371,7 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
         q.lws = ws + sl.lws_off;
         q.lws_each = sl.lws_each;
         q.o_dA = sl.lo.dA;
+        q.o_ctot = sl.lo.ctot;
         q.o_bintra = sl.lo.bintra;
         q.o_bin = sl.lo.bin;
         q.dt0 = dt;
@@ -414,6 +419,7 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
                 p.final_state = layer_states + (size_t)l * state_elems;
                 p.flags = flags & SSD_FLAG_RESIDUAL;
                 p.dA_cum = lws + sl.lo.dA;
+                p.ctot = lws + sl.lo.ctot;
                 p.b_intra = lws + sl.lo.bintra;
                 p.b_in = lws + sl.lo.bin;
                 st = run_layer(p, s, 1, kStages);

@@ -45,7 +45,7 @@ struct Steps {
     size_t act_each;
     unsigned char *lws;        // [depth] layer workspaces of lws_each bytes
     size_t lws_each;
-    size_t o_dA, o_bintra, o_bin;   // offsets inside one layer workspace
+    size_t o_dA, o_bintra, o_bin, o_ctot;   // offsets inside one layer workspace
     const void *dt0, *B0, *C0; // full-sequence dt, B, C
     const float *A0, *D0;      // [n_layers, H]; D0 may be null
     float *states;             // [n_layers, batch, H, P, N]
@@ -68,6 +68,7 @@ struct Problem {
     float *final_state;                      // [batch, H, P, N] or null
     uint32_t flags;
     void *dA_cum;      // [batch, H, nc, Q] of CumT<act>
+    void *ctot;        // [batch, H, nc] of CumT<act>: each chunk's total (its last dA_cum)
     void *b_intra;     // [batch, nc, H, P*N] act dtype, tile order
     void *b_in;        // [batch, nc, H, P*N] tile order, act dtype
     int heads_per_wg_state;   // head group of chunk_state
@@ -123,6 +124,7 @@ __device__ __forceinline__ Problem step_problem(const Problem &p, int k) {
     q.final_state = ls;
     unsigned char *w = st.lws + (size_t)slot * st.lws_each;
     q.dA_cum = w + st.o_dA;
+    q.ctot = w + st.o_ctot;
     q.b_intra = w + st.o_bintra;
     q.b_in = w + st.o_bin;
     return q;

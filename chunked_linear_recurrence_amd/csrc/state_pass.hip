@@ -1,7 +1,7 @@
 // state_pass: the sequential pass of global states across chunks, [分块推理 §2.2] of the
 // page "分块推理：解锁循环模型并行计算，实现长序列高效处理":
 //
-//     b(-1) = init_state (or 0),   b(c) = b_intra(c) + exp(dA_cum[c, last]) * b(c-1)
+//     b(-1) = init_state (or 0),   b(c) = b_intra(c) + exp(total of dA_cum over chunk c) * b(c-1)
 //
 // It writes b_in[c] = b(c-1), the state entering chunk c, and final_state = b(nc-1) in
 // float32.  b_intra and b_in are stored in the activation dtype (what chunk_scan's matrix
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64) void state_pass_kernel(Problem p0) {
     const int64_t cstride = (int64_t)p.H * PN;            // between chunks
     const T *bi = reinterpret_cast<const T *>(p.b_intra) + ((int64_t)b * p.nc * p.H + h) * PN + e;
     T *bo = reinterpret_cast<T *>(p.b_in) + ((int64_t)b * p.nc * p.H + h) * PN + e;
-    const S *cum = reinterpret_cast<const S *>(p.dA_cum) + ((int64_t)b * p.H + h) * p.nc * p.Q + (p.Q - 1);
+    const S *tot = reinterpret_cast<const S *>(p.ctot) + ((int64_t)b * p.H + h) * p.nc;   // chunk totals
     const int nc = p.nc;
 
     V va[K], vb[K];
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64) void state_pass_kernel(Problem p0) {
         for (int u = 0; u < K; ++u)
             if (c0 + u < nc) {                               // uniform
                 v[u] = __builtin_nontemporal_load(reinterpret_cast<const V *>(bi + (int64_t)(c0 + u) * cstride));
-                d[u] = cum[(int64_t)(c0 + u) * p.Q];
+                d[u] = tot[c0 + u];
             }
     };
     auto consume = [&](int c0, const V (&v)[K], const S (&d)[K]) {

@@ -106,8 +106,8 @@ typedef struct ssd_dims {
 
 /* Size in bytes of the workspace ssd_chunk_scan_fwd needs for these dims and chunk_Q,
  * or 0 when the arguments are invalid.  The workspace holds the per-chunk log-decay
- * prefix sums and two per-chunk state buffers (nheads * headdim * dstate * 2 * act bytes /
- * chunk_Q bytes per token). */
+ * prefix sums (with each chunk's total) and two per-chunk state buffers (nheads * headdim *
+ * dstate * 2 * act bytes / chunk_Q bytes per token). */
 size_t ssd_chunk_scan_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q);
 
 /* One layer, the whole sequence [分块推理 §2-§2.2].
