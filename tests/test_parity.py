@@ -243,3 +243,25 @@ def test_head_grouping_does_not_change_the_result(monkeypatch):
         assert torch.equal(y, outs[0][0]) and torch.equal(fin, outs[0][1])
     yr, fr = oracle_layer(d)
     assert err_bf16(outs[0][0], yr) <= 2e-2
+
+
+def _compiled_shapes():
+    try:
+        return [(dt, Q, P, N) for dt in (0, 1) for Q in (32, 64, 128, 256) for P in (16, 32, 64, 128)
+                for N in (16, 32, 64, 128, 256) if ssd.shape_supported(dt, Q, P, N)]
+    except Exception:            # library not built: nothing to parametrize over
+        return []
+
+
+@pytest.mark.parametrize("code,Q,P,N", _compiled_shapes())
+def test_every_compiled_shape(code, Q, P, N):
+    """Every (dtype, Q, P, N) the library compiles, including the largest (P = 128,
+    N = 256) and the single-buffer fp32 ones: three chunks with a ragged tail, two groups,
+    a nonzero initial state."""
+    dtype = "f32" if code == 0 else "bf16"
+    d = small(1, 2 * Q + 5, 4, P, N, 2, dtype, seed=Q * 7 + P + N)
+    y, fin = run_gpu(d, Q)
+    yr, fr = oracle_layer(d)
+    err = err_for(dtype)
+    assert err(y, yr) <= tol_for(dtype), (dtype, Q, P, N)
+    assert err(fin, fr) <= tol_for(dtype), (dtype, Q, P, N)
