@@ -17,9 +17,10 @@
 // every choice that depends on it is a uniform branch.
 //
 // Once per workgroup, each wave computes its causal tiles of S^T = B_c C_c^T on the
-// matrix cores (B fragments straight from L2, C fragments kept in registers), zero above
-// the diagonal, and keeps them in fp32 registers for every head of the group: C.B^T is
-// formed once per chunk and group, never per head.
+// matrix cores (B fragments from the chunk's B tile, staged in LDS by DMA where it fits,
+// else from L2; C fragments kept in registers), zero above the diagonal, and keeps them in
+// fp32 registers for every head of the group: C.B^T is formed once per chunk and group,
+// never per head.
 //
 // Per head, x is brought into LDS by DMA (tokens x channels, read back as transposed
 // fragments), b_in likewise, and the chunk's log-decay prefix sums cum.  The products are
@@ -44,8 +45,9 @@ struct ScanCfg {
     static constexpr int NSLOT = NRB + 2, NPAIR = NSLOT / 2;
     static constexpr int NTRI = NRB * (NRB + 1) / 2;            // causal tiles per chunk
     static constexpr int PT = P / 16, NT = N / 16;
+    // one head's inputs in LDS: x tile, b(c-1) tile, cum row (the layout of HeadBuf)
     static constexpr int HEAD_BYTES = Q * P * (int)sizeof(T) + P * N * (int)sizeof(T) +
-                                      Q * (int)sizeof(typename CumT<T>::type) + 2 * Q * 4;
+                                      Q * (int)sizeof(typename CumT<T>::type);
     static constexpr bool DB = 2 * HEAD_BYTES <= kLdsBytes;     // double-buffered head data
     static constexpr int YPIECES = P * (int)sizeof(T) / 16;      // 16-byte pieces per output row
     static constexpr int YW = 32 * P * (int)sizeof(T);           // one wave's staged outputs
@@ -355,6 +357,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         }
     };
     static_assert(CP <= THREADS, "cum fits one DMA item");
+    static_assert(Buf::BYTES == Cfg::HEAD_BYTES, "head buffer layout and LDS sizing agree");
     // the x, state and B pieces always fill whole waves, so their guards are uniform
     static_assert((Q * XPIECES) % 64 == 0 && SP % 64 == 0 && (Q * Cfg::BPIECES) % 64 == 0,
                   "x, state and B tiles are whole waves of 16-byte pieces");
