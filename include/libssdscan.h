@@ -51,6 +51,11 @@
  *   256} (bfloat16 needs dstate >= 32); the set actually compiled is reported by
  *   ssd_shape_supported().  Any batch, seqlen >= 1, nheads >= 1 with nheads % ngroups == 0.
  *   A must be finite.  The last chunk may be shorter than Q.
+ *
+ * Tuning (environment, read at each call; optional): SSD_HEADS_PER_WG_STATE and
+ *   SSD_HEADS_PER_WG_SCAN set how many heads one workgroup of chunk_state / chunk_scan
+ *   processes (by default chosen from the problem size).  They change only how the work
+ *   is split, never the arithmetic: results are bit-identical for every value.
  */
 #ifndef LIBSSDSCAN_H
 #define LIBSSDSCAN_H
