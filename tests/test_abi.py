@@ -175,3 +175,14 @@ def test_scan_form_flag_validation():
     assert L.ssd_chunk_scan_segmented(ctypes.byref(d), 2, 128, v(FAKE), v(FAKE + 2 ** 30), v(FAKE + 2 ** 31),
                                       v(FAKE + 2 ** 32), v(FAKE + 2 ** 33), None, v(FAKE + 2 ** 36), 64, 4,
                                       v(FAKE + 2 ** 34), v(FAKE + 2 ** 35), 1 << 30, None) == 2
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library the binding raises; there is no fallback path."""
+    monkeypatch.setattr(ssd, "_lib", None)
+    monkeypatch.setattr(ssd, "LIB_PATH", str(tmp_path / "libssdscan.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        ssd.lib()
+    with pytest.raises(RuntimeError):
+        ssd.fwd(torch.zeros(1, 4, 1, 16), torch.zeros(1, 4, 1), torch.zeros(1), torch.zeros(1, 4, 1, 16),
+                torch.zeros(1, 4, 1, 16), None, None, 64)
