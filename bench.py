@@ -13,6 +13,7 @@ Besides the headline tokens/s the line carries:
                 runs on, inside full steps) against the 8 TB/s peak;
   kernels       the same figures for all four kernels, plus matrix-core rates;
   end_to_end    the method's bytes / step time against peak HBM bandwidth;
+  workloads     one step of the smaller bf16 workloads (cache evicted before each);
   scan_form     the chunk outputs computed by the associative-scan kernel instead of the
                 matrix-core one (same layer), for comparison;
   decode        the decode step (ssd_step) at the same layer shape, batch 1 and 8;
@@ -52,6 +53,8 @@ def parse():
                     help="skip the secondary timing of the 24-layer vertical stack")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary timing of the decode step")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the secondary timing of the smaller bf16 workloads")
     ap.add_argument("--no-scan-form", action="store_true",
                     help="skip the secondary timing of the associative-scan form of the chunk outputs")
     ap.add_argument("--kernel-steps", type=int, default=0, help="launches per kernel for per-kernel timing "
@@ -197,6 +200,44 @@ def decode_timing(torch, dev, steps=200):
     return out
 
 
+def workload_timing(torch, dev, reps=10):
+    """One step of each smaller bf16 workload (the Mamba-2-130M layer, the batch-8
+    throughput layer).  Their data fits the 256 MB last-level cache, so a 1 GiB buffer is
+    written before every timed step (outside the HIP events around it): the step then
+    reads its inputs from HBM, as the large workload does."""
+    from chunked_linear_recurrence_amd import inputs, ssd, WORKLOADS
+    evict = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("mamba2_130m_layer_b2_L2048", "throughput_b8_L4096_h32"):
+        w = WORKLOADS[name]
+        d = inputs.make(w)
+        g = {k: (v.to(dev) if v is not None else None) for k, v in d.items()}
+        dims = ssd.dims_of(g["x"], g["B"])
+        ws = ssd.alloc_workspace(ssd.workspace_bytes(dims, w.chunk), dev)
+        y = torch.empty_like(g["x"])
+        fin = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, device=dev)
+
+        def step():
+            ssd.fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["init_state"], w.chunk, y=y,
+                    final_state=fin, workspace=ws, stream=stream)
+        for _ in range(5):
+            step()
+        times = []
+        for _ in range(reps):
+            evict.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        out[name] = {"ms_per_step_median": round(ms, 4), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1)}
+    del evict
+    return out
+
+
 def cpu_baseline(d, w):
     """The fp64 oracle (plain C, one thread per (batch, head) pair) on this host."""
     import numpy as np
@@ -320,6 +361,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+    if not args.no_workloads:
+        print("[bench] smaller workloads", file=sys.stderr, flush=True)
+        out["workloads"] = workload_timing(torch, dev)
     if not args.no_scan_form:
         print("[bench] scan form", file=sys.stderr, flush=True)
         sf = {"workload": w.name, "stage": "chunk outputs (stage 4)"}
