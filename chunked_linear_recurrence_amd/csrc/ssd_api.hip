@@ -150,8 +150,11 @@ ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q, int steps =
     p.dtype = d.dtype;
     const int64_t units = d.batch * p.nc * d.ngroups * steps;
     const int64_t hpg = d.nheads / d.ngroups;
+    // chunk_scan takes most of a CU's LDS (one workgroup per CU): aim for about one
+    // workgroup per CU, which amortises each workgroup's C.B^T tiles over as many heads as
+    // that allows.  chunk_state (two workgroups per CU) measured best with about four per CU.
     p.heads_per_wg_state = heads_per_wg(units, hpg, 1024, "SSD_HEADS_PER_WG_STATE");
-    p.heads_per_wg_scan = heads_per_wg(units, hpg, 512, "SSD_HEADS_PER_WG_SCAN");
+    p.heads_per_wg_scan = heads_per_wg(units, hpg, 256, "SSD_HEADS_PER_WG_SCAN");
     return p;
 }
 
