@@ -10,15 +10,18 @@
 // Sums are float64 for float32 activations (dt * A is then exact) and float32 for
 // bfloat16 activations.
 //
-// Work: one workgroup (4 wave64) per (batch, chunk, block of 16 heads).  The Q x 16 tile
-// of dt * A is staged in LDS with coalesced loads; each wave then scans one head at a
-// time: every lane sums Q/64 consecutive values, and a 6-step wave shuffle scan combines
-// the lane totals.  HBM-bound (reads dt once, writes 4 bytes per token-head).
+// Work: one workgroup per (batch, chunk, block of kCumHeads heads), one wave per head.  The
+// Q x kCumHeads tile of dt * A is staged in LDS with coalesced loads; each wave then scans
+// its head: every lane sums Q/64 consecutive values, and a 6-step wave shuffle scan
+// combines the lane totals.  HBM-bound (reads dt once, writes 4 bytes per token-head).
 #include "ssd_common.h"
 
 namespace ssd {
 
-constexpr int kCumHeads = 16;
+// Heads per workgroup (the Q x heads tile of dt * A staged in LDS) and threads: one wave
+// per head, so each wave runs a single scan (measured fastest: 8 heads x 8 waves, against 16
+// heads x 4 waves with four scans per wave, or whole 64-head token rows).
+constexpr int kCumHeads = 8, kCumThreads = kCumHeads * 64;
 
 // A lane's E consecutive values as one vector store (E * sizeof(V) bytes).
 template <typename V, int E>
@@ -41,7 +44,7 @@ __device__ __forceinline__ void store_run(V *dst, const V (&v)[E]) {
 }
 
 template <typename T, int Q>
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
+__global__ __launch_bounds__(kCumThreads) void chunk_cumsum_kernel(Problem p0) {
     typedef typename CumT<T>::type S;
     constexpr int E = Q >= 64 ? Q / 64 : 1;      // values per lane
     constexpr int NA = Q / E;                    // lanes holding tokens (64, or Q when Q < 64)
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
     const T *dt = reinterpret_cast<const T *>(p.dt) + (int64_t)b * p.dt_bs;
     const int nh = min(kCumHeads, p.H - hb);
 
-    for (int idx = threadIdx.x; idx < Q * kCumHeads; idx += 256) {
+    for (int idx = threadIdx.x; idx < Q * kCumHeads; idx += kCumThreads) {
         const int j = idx / kCumHeads, hh = idx % kCumHeads;
         S v = 0;
         if (hh < nh && j < Qc) v = (S)to_f32(dt[(int64_t)(t0 + j) * p.H + hb + hh]) * (S)p.A[hb + hh];
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool active = lane < NA;
-    for (int hh = wave; hh < nh; hh += 4) {
+    for (int hh = wave; hh < nh; hh += kCumThreads / 64) {
         S v[E];
         S run = 0;
 #pragma unroll
@@ -104,16 +107,16 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Problem p0) {
 hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s) {
     dim3 grid(p.nc, (p.H + kCumHeads - 1) / kCumHeads, p.batch * step_count(p));
     if (p.dtype == 1) {
-        if (p.Q == 32) chunk_cumsum_kernel<bf16, 32><<<grid, 256, 0, s>>>(p);
-        else if (p.Q == 64) chunk_cumsum_kernel<bf16, 64><<<grid, 256, 0, s>>>(p);
-        else if (p.Q == 128) chunk_cumsum_kernel<bf16, 128><<<grid, 256, 0, s>>>(p);
-        else if (p.Q == 256) chunk_cumsum_kernel<bf16, 256><<<grid, 256, 0, s>>>(p);
+        if (p.Q == 32) chunk_cumsum_kernel<bf16, 32><<<grid, kCumThreads, 0, s>>>(p);
+        else if (p.Q == 64) chunk_cumsum_kernel<bf16, 64><<<grid, kCumThreads, 0, s>>>(p);
+        else if (p.Q == 128) chunk_cumsum_kernel<bf16, 128><<<grid, kCumThreads, 0, s>>>(p);
+        else if (p.Q == 256) chunk_cumsum_kernel<bf16, 256><<<grid, kCumThreads, 0, s>>>(p);
         else return hipErrorInvalidValue;
     } else {
-        if (p.Q == 32) chunk_cumsum_kernel<float, 32><<<grid, 256, 0, s>>>(p);
-        else if (p.Q == 64) chunk_cumsum_kernel<float, 64><<<grid, 256, 0, s>>>(p);
-        else if (p.Q == 128) chunk_cumsum_kernel<float, 128><<<grid, 256, 0, s>>>(p);
-        else if (p.Q == 256) chunk_cumsum_kernel<float, 256><<<grid, 256, 0, s>>>(p);
+        if (p.Q == 32) chunk_cumsum_kernel<float, 32><<<grid, kCumThreads, 0, s>>>(p);
+        else if (p.Q == 64) chunk_cumsum_kernel<float, 64><<<grid, kCumThreads, 0, s>>>(p);
+        else if (p.Q == 128) chunk_cumsum_kernel<float, 128><<<grid, kCumThreads, 0, s>>>(p);
+        else if (p.Q == 256) chunk_cumsum_kernel<float, 256><<<grid, kCumThreads, 0, s>>>(p);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();
