@@ -265,3 +265,19 @@ def test_every_compiled_shape(code, Q, P, N):
     err = err_for(dtype)
     assert err(y, yr) <= tol_for(dtype), (dtype, Q, P, N)
     assert err(fin, fr) <= tol_for(dtype), (dtype, Q, P, N)
+
+
+@pytest.mark.parametrize("b,L,H,G,dtype", [
+    (33, 300, 3, 1, "bf16"),      # large odd batch, three heads
+    (5, 700, 20, 4, "bf16"),      # heads split unevenly over cumsum blocks and head groups
+    (2, 1100, 96, 2, "bf16"),     # many heads
+    (17, 150, 5, 5, "f32"),       # fp32, one head per group, every chunk short
+])
+def test_batch_and_head_counts(b, L, H, G, dtype):
+    Q, P, N = (256, 64, 128) if dtype == "bf16" else (64, 32, 64)
+    d = small(b, L, H, P, N, G, dtype, seed=b * 100 + H)
+    y, fin = run_gpu(d, Q)
+    yr, fr = oracle_layer(d)
+    err = err_for(dtype)
+    assert err(y, yr) <= tol_for(dtype)
+    assert err(fin, fr) <= tol_for(dtype)
