@@ -532,9 +532,8 @@ static hipError_t launch_scan_t(const Problem &p, hipStream_t s) {
     if constexpr (!Cfg::OK) {
         return hipErrorInvalidValue;
     } else {
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void *)chunk_scan_kernel<T, Q, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-        if (attr != hipSuccess) return attr;
+        if (const hipError_t attr = allow_lds<chunk_scan_kernel<T, Q, P, N>>(Cfg::LDS); attr != hipSuccess)
+            return attr;
         const int hpg = p.H / p.G;
         const int nhg = p.G * ((hpg + p.heads_per_wg_scan - 1) / p.heads_per_wg_scan);
         const int64_t nblk = (int64_t)p.batch * p.nc * nhg;

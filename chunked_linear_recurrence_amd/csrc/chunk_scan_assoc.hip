@@ -204,9 +204,8 @@ static hipError_t launch_assoc_t(const Problem &p, hipStream_t s) {
     if constexpr (!Cfg::OK) {
         return hipErrorInvalidValue;
     } else {
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void *)chunk_scan_assoc_kernel<T, Q, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-        if (attr != hipSuccess) return attr;
+        if (const hipError_t attr = allow_lds<chunk_scan_assoc_kernel<T, Q, P, N>>(Cfg::LDS); attr != hipSuccess)
+            return attr;
         const int64_t nblk = (int64_t)p.batch * p.nc * p.H;
         if (nblk <= 0 || nblk > 0x7fffffff) return hipErrorInvalidValue;
         chunk_scan_assoc_kernel<T, Q, P, N><<<dim3((unsigned)nblk, step_count(p)), Cfg::THREADS, Cfg::LDS, s>>>(p);

@@ -226,9 +226,8 @@ static hipError_t launch_state_t(const Problem &p, hipStream_t s) {
         const int nhg = p.G * ((hpg + p.heads_per_wg_state - 1) / p.heads_per_wg_state);
         const int64_t nblk = (int64_t)p.batch * p.nc * nhg;
         if (nblk <= 0 || nblk > 0x7fffffff) return hipErrorInvalidValue;
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void *)chunk_state_kernel<T, Q, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-        if (attr != hipSuccess) return attr;
+        if (const hipError_t attr = allow_lds<chunk_state_kernel<T, Q, P, N>>(Cfg::LDS); attr != hipSuccess)
+            return attr;
         chunk_state_kernel<T, Q, P, N><<<dim3((unsigned)nblk, step_count(p)), Cfg::THREADS, Cfg::LDS, s>>>(p);
         return hipGetLastError();
     }

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace ssd {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -145,6 +147,22 @@ struct StepArgs {
 };
 
 hipError_t launch_ssd_step(const StepArgs &a, hipStream_t s);
+
+// Lets Kernel use `bytes` of dynamic LDS (beyond the 64 KB default) on the current device.
+// The attribute is per device, so it is set once per (kernel, device): a process may call
+// the library on several GPUs.
+template <auto Kernel>
+inline hipError_t allow_lds(int bytes) {
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute((const void *)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 bool step_supported(int dstate);
 hipError_t launch_chunk_cumsum(const Problem &p, hipStream_t s);
 hipError_t launch_chunk_state(const Problem &p, hipStream_t s);
