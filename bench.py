@@ -193,8 +193,29 @@ def decode_timing(torch, dev, steps=200):
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / steps * 1e3
+        # the same steps captured once in a HIP graph and replayed (launch cost amortised)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for t in range(steps):
+                x, dt, B, C = toks[t]
+                ssd.step(x, dt, g["A"], B, C, g["D"], state, y=y)
+        stream.wait_stream(side)
+        with torch.cuda.graph(graph):
+            for t in range(steps):
+                x, dt, B, C = toks[t]
+                ssd.step(x, dt, g["A"], B, C, g["D"], state, y=y)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_graph = e0.elapsed_time(e1) / steps * 1e3
         sbytes = 2 * state.numel() * 4
         out.append({"batch": b, "nheads": 48, "headdim": 64, "dstate": 128, "us_per_step": round(us, 2),
+                    "us_per_step_graph": round(us_graph, 2),
                     "tokens_per_s": round(b / (us * 1e-6), 1), "state_bytes_per_step": sbytes,
                     "state_GB_s": round(sbytes / (us * 1e-6) / 1e9, 1)})
     return out

@@ -33,8 +33,10 @@
  *   returns without waiting.  Argument errors are detected on the host before anything
  *   is enqueued, and then nothing is written.  A fault inside a kernel surfaces at the
  *   caller's next synchronisation.  No C++ exception crosses this interface.
- *   The library holds no global mutable state except a per-thread error message, so
- *   concurrent calls on different workspaces are safe.
+ *   The library holds no global mutable state except a per-thread error message (and a
+ *   once-per-device kernel attribute), so concurrent calls on different workspaces are
+ *   safe.  No entry point allocates or synchronises, so calls can be captured in HIP
+ *   graphs.
  *
  * Layouts (row-major, contiguous, element types in parentheses; "act" = the dims' dtype)
  *   x, y             [batch, seqlen, nheads, headdim]          (act)
