@@ -12,7 +12,9 @@ Besides the headline tokens/s the line carries:
                 its mean duration, from HIP events around each launch on the stream it
                 runs on, inside full steps) against the 8 TB/s peak;
   kernels       the same figures for all four kernels, plus matrix-core rates;
-  end_to_end    the method's bytes / step time against peak HBM bandwidth;
+  end_to_end    the method's bytes / step time against peak HBM bandwidth, with the
+                bytes per stored per-chunk state element (state_bytes) and the same rate
+                on the compulsory bytes alone;
   workloads     one step of the smaller bf16 workloads (cache evicted before each);
   scan_form     the chunk outputs computed by the associative-scan kernel instead of the
                 matrix-core one (same layer), for comparison;
@@ -66,8 +68,10 @@ def parse():
 
 def alg_bytes(w):
     """Bytes each kernel must move once per launch (every input it reads and every output
-    it writes, once, in the dtype the library stores it), and the method's bytes: the
-    compulsory activations and states plus the per-chunk state exchange."""
+    it writes, once, in the dtype the library stores it); the method's bytes: the
+    compulsory activations and states plus the per-chunk state exchange (b_intra and b_in
+    each written and read once, in the activation dtype); and the compulsory bytes alone
+    (x, y, dt, B, C, and the initial and final states)."""
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     e = w.act_bytes
     nc = w.nchunks
@@ -85,8 +89,9 @@ def alg_bytes(w):
         "state_pass": 2 * states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
         "chunk_scan": x + 2 * bc + cum + states * e + y,
     }
-    method = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final + 4 * states * e
-    return k, method
+    compulsory = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final
+    method = compulsory + 4 * states * e
+    return k, method, compulsory
 
 
 def alg_flops(w):
@@ -334,7 +339,7 @@ def main():
     # on the same stream with a HIP event between consecutive kernels, so each kernel is
     # timed where it runs inside a step (after its producer, before its consumer).
     names = ["chunk_cumsum", "chunk_state", "state_pass", "chunk_scan"]
-    kb, method_bytes = alg_bytes(w)
+    kb, method_bytes, compulsory_bytes = alg_bytes(w)
     kf = alg_flops(w)
     ksteps = args.kernel_steps or args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(ksteps)]
@@ -362,6 +367,7 @@ def main():
             "unit": "GB/s", "frac": kernels[dom]["hbm_frac"], "traffic": measured_traffic(w.name, dom),
             "alg_bytes_per_launch": kb[dom], "mean_launch_us": kernels[dom]["us"]}
     e2e_gbs = method_bytes / (ms_step * 1e-3) / 1e9
+    comp_gbs = compulsory_bytes / (ms_step * 1e-3) / 1e9
 
     out = {
         "metric": "SSD chunked-scan tokens/s per GPU; % of bf16 MFMA peak and % of HBM BW",
@@ -372,8 +378,11 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk": w.chunk},
         "roofline": roof,
-        "end_to_end": {"method_bytes": method_bytes, "GB_s": round(e2e_gbs, 1),
-                       "hbm_frac": round(e2e_gbs / HBM_PEAK_GBS, 4)},
+        "end_to_end": {"method_bytes": method_bytes, "state_bytes": w.act_bytes,
+                       "GB_s": round(e2e_gbs, 1), "hbm_frac": round(e2e_gbs / HBM_PEAK_GBS, 4),
+                       "compulsory_bytes": compulsory_bytes,
+                       "compulsory_GB_s": round(comp_gbs, 1),
+                       "compulsory_hbm_frac": round(comp_gbs / HBM_PEAK_GBS, 4)},
         "kernels": kernels,
         "ms_per_step_staged": round(staged_ms, 4),
         "wall_s_timed": round(wall, 4),

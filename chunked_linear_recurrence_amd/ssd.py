@@ -96,6 +96,96 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+_ACT_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _expect(name, t, shape, dtypes, allow_none=False):
+    """Raise ValueError unless tensor `t` has exactly `shape` (None entries match any
+    size), one of `dtypes` and a contiguous layout.  The C side sees only raw pointers,
+    so this is the one place where a wrong dtype, shape or stride can be caught."""
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor (got %s)" % (name, type(t).__name__))
+    if t.dim() != len(shape) or any(s is not None and s != d for s, d in zip(shape, t.shape)):
+        raise ValueError("%s has shape %s; expected %s" % (
+            name, tuple(t.shape), tuple("*" if s is None else s for s in shape)))
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s; expected %s" % (
+            name, t.dtype, " or ".join(str(d) for d in dtypes)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _same_device(**tensors):
+    """All tensors on one CUDA device (checked after shapes and dtypes)."""
+    devs = {n: t.device for n, t in tensors.items() if t is not None}
+    for n, d in devs.items():
+        if d.type != "cuda":
+            raise ValueError("%s is on %s; every tensor must be on a CUDA device" % (n, d))
+    if len(set(devs.values())) > 1:
+        raise ValueError("tensors are on different devices: %s" % (
+            ", ".join("%s %s" % (n, d) for n, d in devs.items())))
+
+
+def check_layer_args(x, dt, A, B, C, D=None, init_state=None, y=None, final_state=None, workspace=None):
+    """Shapes, dtypes, contiguity and device of one layer's tensors (ssd_chunk_scan_fwd):
+    x [b, L, H, P], dt [b, L, H], B and C [b, L, G, N], all of one activation dtype
+    (float32 or bfloat16), y like x; A and D [H] float32; init_state and final_state
+    [b, H, P, N] float32; all contiguous and on one CUDA device."""
+    _expect("x", x, (None, None, None, None), _ACT_DTYPES)
+    b, L, H, P = x.shape
+    _expect("B", B, (b, L, None, None), (x.dtype,))
+    G, N = B.shape[2], B.shape[3]
+    _expect("dt", dt, (b, L, H), (x.dtype,))
+    _expect("C", C, (b, L, G, N), (x.dtype,))
+    _expect("A", A, (H,), (torch.float32,))
+    _expect("D", D, (H,), (torch.float32,), allow_none=True)
+    _expect("init_state", init_state, (b, H, P, N), (torch.float32,), allow_none=True)
+    _expect("y", y, (b, L, H, P), (x.dtype,), allow_none=True)
+    _expect("final_state", final_state, (b, H, P, N), (torch.float32,), allow_none=True)
+    _expect("workspace", workspace, (None,), (torch.uint8,), allow_none=True)
+    _same_device(x=x, dt=dt, A=A, B=B, C=C, D=D, init_state=init_state, y=y,
+                 final_state=final_state, workspace=workspace)
+
+
+def check_stack_args(x0, dt, A, B, C, D, layer_states, y=None, workspace=None):
+    """As check_layer_args for the stack (ssd_chunk_scan_segmented): A and D are
+    [n_layers, H] float32 and layer_states [n_layers, b, H, P, N] float32."""
+    _expect("x0", x0, (None, None, None, None), _ACT_DTYPES)
+    b, L, H, P = x0.shape
+    _expect("B", B, (b, L, None, None), (x0.dtype,))
+    G, N = B.shape[2], B.shape[3]
+    _expect("dt", dt, (b, L, H), (x0.dtype,))
+    _expect("C", C, (b, L, G, N), (x0.dtype,))
+    _expect("A", A, (None, H), (torch.float32,))
+    nl = A.shape[0]
+    _expect("D", D, (nl, H), (torch.float32,), allow_none=True)
+    _expect("layer_states", layer_states, (nl, b, H, P, N), (torch.float32,))
+    _expect("y", y, (b, L, H, P), (x0.dtype,), allow_none=True)
+    _expect("workspace", workspace, (None,), (torch.uint8,), allow_none=True)
+    _same_device(x0=x0, dt=dt, A=A, B=B, C=C, D=D, layer_states=layer_states, y=y,
+                 workspace=workspace)
+
+
+def check_step_args(x, dt, A, B, C, D, state, y=None):
+    """As check_layer_args for one decode token (ssd_step): x [b, H, P], dt [b, H],
+    B and C [b, G, N], A and D [H], state [b, H, P, N] float32."""
+    _expect("x", x, (None, None, None), _ACT_DTYPES)
+    b, H, P = x.shape
+    _expect("B", B, (b, None, None), (x.dtype,))
+    G, N = B.shape[1], B.shape[2]
+    _expect("dt", dt, (b, H), (x.dtype,))
+    _expect("C", C, (b, G, N), (x.dtype,))
+    _expect("A", A, (H,), (torch.float32,))
+    _expect("D", D, (H,), (torch.float32,), allow_none=True)
+    _expect("state", state, (b, H, P, N), (torch.float32,))
+    _expect("y", y, (b, H, P), (x.dtype,), allow_none=True)
+    _same_device(x=x, dt=dt, A=A, B=B, C=C, D=D, state=state, y=y)
+
+
 def dims_of(x, B, dtype=None):
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -138,7 +228,13 @@ def fwd(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y=None, final_sta
         residual=False, workspace=None, stream=None, want_final=True, first_stage=1, last_stage=NSTAGES,
         scan_form=False):
     """One layer over the whole sequence (ssd_chunk_scan_fwd).  Returns (y, final_state).
-    scan_form=True computes the chunk outputs with the associative-scan kernel."""
+    scan_form=True computes the chunk outputs with the associative-scan kernel.
+
+    The decay a_t = exp(dt A) must lie in [0, 1]: dt >= 0 and A <= 0 (the library's
+    contract; other values give unspecified results).  Tensor shapes, dtypes, contiguity
+    and device are checked here (ValueError), values are not."""
+    lib()                  # fails loudly when the library is not built
+    check_layer_args(x, dt, A, B, C, D, init_state, y, final_state, workspace)
     dims = dims_of(x, B)
     nbytes = workspace_bytes(dims, chunk)
     if nbytes == 0:
@@ -164,7 +260,10 @@ def fwd(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y=None, final_sta
 def segmented(x0, dt, A, B, C, D, layer_states, V, chunk=256, *, y=None, residual=True,
               wavefront=True, workspace=None, stream=None):
     """Vertical layer stack (ssd_chunk_scan_segmented); layer_states is updated in place.
-    wavefront=False runs the (segment, layer) steps strictly one at a time."""
+    wavefront=False runs the (segment, layer) steps strictly one at a time.  As for fwd,
+    dt >= 0 and A <= 0."""
+    lib()                  # fails loudly when the library is not built
+    check_stack_args(x0, dt, A, B, C, D, layer_states, y, workspace)
     dims = dims_of(x0, B)
     n_layers = A.shape[0]
     nbytes = segmented_workspace_bytes(dims, chunk, V, n_layers, wavefront)
@@ -181,6 +280,8 @@ def segmented(x0, dt, A, B, C, D, layer_states, V, chunk=256, *, y=None, residua
 
 def horizontal(x0, dt, A, B, C, D, layer_states, chunk=256, *, residual=True, stream=None):
     """Layer-serial stack: ssd_chunk_scan_fwd once per layer over the whole sequence."""
+    lib()                  # fails loudly when the library is not built
+    check_stack_args(x0, dt, A, B, C, D, layer_states)
     u = x0
     dims = dims_of(x0, B)
     ws = alloc_workspace(workspace_bytes(dims, chunk), x0.device)
@@ -195,7 +296,9 @@ def horizontal(x0, dt, A, B, C, D, layer_states, chunk=256, *, residual=True, st
 
 def step(x, dt, A, B, C, D, state, *, y=None, residual=False, stream=None):
     """One decode step (ssd_step): x [b, H, P], dt [b, H], B/C [b, G, N]; state [b, H, P, N]
-    float32 is updated in place.  Returns y [b, H, P]."""
+    float32 is updated in place.  Returns y [b, H, P].  As for fwd, dt >= 0 and A <= 0."""
+    lib()                  # fails loudly when the library is not built
+    check_step_args(x, dt, A, B, C, D, state, y)
     b, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     dtype = SSD_BF16 if x.dtype == torch.bfloat16 else SSD_F32

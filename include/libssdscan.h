@@ -52,7 +52,17 @@
  *   chunk_Q in {32, 64, 128, 256}; headdim in {16, 32, 64, 128}; dstate in {16, 32, 64, 128,
  *   256} (bfloat16 needs dstate >= 32); the set actually compiled is reported by
  *   ssd_shape_supported().  Any batch, seqlen >= 1, nheads >= 1 with nheads % ngroups == 0.
- *   A must be finite.  The last chunk may be shorter than Q.
+ *   The last chunk may be shorter than Q.
+ *
+ * Values: every a_t must be a decay, 0 <= a_t <= 1, i.e. dt >= 0 and A <= 0, both finite
+ *   (as the state transition of [分块推理 §2] is in every workload).  The kernels rely on
+ *   it: the log-decay prefix sums of dt * A never increase along a chunk, so every decay
+ *   they form between two tokens is exp of a non-positive number (the diagonal tiles of
+ *   ssd_chunk_scan_fwd clamp that exponent at 0 to mask the tokens after i).  With a
+ *   growing a_t (dt * A > 0) the results are unspecified: they are wrong, and may
+ *   overflow.  The library cannot check device-resident values without synchronising, so
+ *   it does not; this contract applies to ssd_chunk_scan_fwd, ssd_chunk_scan_stages,
+ *   ssd_chunk_scan_segmented and ssd_step.
  *
  * Tuning (environment, read at each call; optional): SSD_HEADS_PER_WG_STATE and
  *   SSD_HEADS_PER_WG_SCAN set how many heads one workgroup of chunk_state / chunk_scan

@@ -195,6 +195,93 @@ def test_chunk_states_compose():
         assert _rel(o["b_in"][:, c], fin) < 1e-12
 
 
+def _intermediate_mismatches(o, prob, Q):
+    """Names of the chunked intermediates in `o` that differ from a computation sharing no
+    step with the decomposition [分块推理 §2.1-§2.2]:
+      b_intra(c)  = final state of the sequential recurrence run from a zero state over
+                    chunk c's tokens alone;
+      by_intra(c) = that run's output without the skip term;
+      logcum      = numpy's cumulative sum of dt * A within each chunk (NaN past the end);
+      b_in(c)     = final state of the recurrence run from init_state over tokens [0, cQ);
+      by_inter_i  = (product of exp(dt A) from the chunk start to token i, by np.prod)
+                    times C_i contracted with b_in(c)."""
+    x, dt, A, B, C, D, init = prob
+    b, L, H, P = x.shape
+    G = B.shape[2]
+    bad = set()
+    for c in range(-(-L // Q)):
+        t0, t1 = c * Q, min(c * Q + Q, L)
+        sl = slice(t0, t1)
+        y0, f0 = oracle.seq(x[:, sl], dt[:, sl], A, B[:, sl], C[:, sl], None, None)
+        if _rel(o["b_intra"][:, c], f0) > 1e-12:
+            bad.add("b_intra")
+        if _rel(o["by_intra"][:, sl], y0) > 1e-12:
+            bad.add("by_intra")
+        if c == 0:
+            ref_in = init
+        else:
+            _, ref_in = oracle.seq(x[:, :t0], dt[:, :t0], A, B[:, :t0], C[:, :t0], D, init)
+        if _rel(o["b_in"][:, c], ref_in) > 1e-12:
+            bad.add("b_in")
+        for bb in range(b):
+            for h in range(H):
+                ref = np.cumsum(dt[bb, sl, h] * A[h])
+                lc = o["logcum"][bb, h, c]
+                if not (np.allclose(lc[:t1 - t0], ref, rtol=1e-13, atol=1e-15)
+                        and np.isnan(lc[t1 - t0:]).all()):
+                    bad.add("logcum")
+                g = h // (H // G)
+                a = np.exp(dt[bb, sl, h] * A[h])
+                for i, t in enumerate(range(t0, t1)):
+                    ref = np.prod(a[:i + 1]) * (ref_in[bb, h] @ C[bb, t, g])
+                    if not np.allclose(o["by_inter"][bb, t, h], ref, rtol=1e-12, atol=1e-14):
+                        bad.add("by_inter")
+    return bad
+
+
+def _intermediates_problem(Q):
+    rng = np.random.default_rng(40 + Q)
+    return _random_problem(rng, 2, 23, 4, 3, 5, 2)      # b 2, L 23, H 4 in 2 groups, P 3, N 5
+
+
+@pytest.mark.parametrize("Q", [4, 5, 9])
+def test_chunked_intermediates_against_per_chunk_runs(Q):
+    """Every intermediate oracle.chunked exports, at batch 2, 4 heads in 2 groups, P = 3,
+    N = 5, a nonzero initial state and a ragged last chunk, equals its independent
+    computation (_intermediate_mismatches)."""
+    prob = _intermediates_problem(Q)
+    o = oracle.chunked(*prob, Q)
+    nc = -(-23 // Q)
+    assert o["b_intra"].shape == (2, nc, 4, 3, 5) and o["logcum"].shape == (2, 4, nc, Q)
+    assert _intermediate_mismatches(o, prob, Q) == set()
+
+
+def test_intermediates_pin_catches_planted_index_slips():
+    """Index slips planted in a copy of the oracle's exports (on the CPU): heads swapped,
+    batch rows swapped, chunk index shifted, a transposed P x N state, an exclusive
+    prefix.  Each is seen by the per-chunk pin above."""
+    Q = 5
+    prob = _intermediates_problem(Q)
+    o = oracle.chunked(*prob, Q)
+    plants = {
+        "b_intra": lambda o: o["b_intra"][:, :, [1, 0, 2, 3]],                    # heads
+        "b_in": lambda o: np.concatenate([o["b_in"][:, 1:], o["b_in"][:, -1:]], 1),  # chunk + 1
+        "by_intra": lambda o: o["by_intra"][::-1],                               # batch rows
+        "logcum": lambda o: np.concatenate([np.zeros_like(o["logcum"][..., :1]),
+                                            o["logcum"][..., :-1]], -1),        # exclusive
+        "by_inter": lambda o: o["by_inter"][:, :, [0, 1, 3, 2]],                  # heads
+    }
+    for name, plant in plants.items():
+        bad = dict(o)
+        bad[name] = np.ascontiguousarray(plant(o))
+        assert name in _intermediate_mismatches(bad, prob, Q), name
+    # a transposed state (P = 3, N = 5 read as N x P) cannot even keep its shape
+    t = o["b_intra"].reshape(2, -1, 4, 5, 3).swapaxes(-1, -2)
+    assert not np.array_equal(t, o["b_intra"])
+    bad = dict(o, b_intra=np.ascontiguousarray(t))
+    assert "b_intra" in _intermediate_mismatches(bad, prob, Q)
+
+
 # ------------------------------------------------------- P3: a == 1 is a prefix sum
 
 def test_a_equal_one_is_prefix_sum():

@@ -2,8 +2,8 @@
 
 Same seeded inputs on both sides; every comparison is element by element, at the
 tolerance of the activation dtype (see helpers.py).  Sizes span several chunks and a
-ragged last chunk; the named workloads run at their full sizes (the 128K-token one is
-compared on sampled heads over the whole sequence).
+ragged last chunk; the named workloads run at their full sizes, every output element
+compared.
 """
 import math
 
@@ -42,12 +42,16 @@ def small(batch, L, H, P, N, G, dtype, seed, init=True, dt_max=0.1):
 
 # --------------------------------------------------------------------- per stage
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_stages_match_oracle_intermediates(dtype):
+@pytest.mark.parametrize("dtype,b,L,H,P,N,G,Q", [
+    ("f32", 2, 3 * 64 + 17, 4, 32, 64, 2, 64),
+    ("bf16", 2, 3 * 64 + 17, 4, 32, 64, 2, 64),
+    ("bf16", 2, 3 * 256 + 37, 3, 64, 128, 1, 256),     # the shape of the 128K-token layer
+    ("f32", 2, 2 * 256 + 9, 2, 64, 128, 1, 256),
+])
+def test_stages_match_oracle_intermediates(dtype, b, L, H, P, N, G, Q):
     """dA_cum, b_intra and b_in left in the workspace match the oracle's chunked
     decomposition (logcum, b_intra, b_in) of [分块推理 §2.1-§2.2]."""
-    b, L, H, P, N, G, Q = 2, 3 * 64 + 17, 4, 32, 64, 2, 64
-    d = small(b, L, H, P, N, G, dtype, seed=5)
+    d = small(b, L, H, P, N, G, dtype, seed=5 + Q)
     ref = oracle.chunked(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], Q)
     g = to_dev(d, DEV)
     dims = ssd.dims_of(g["x"], g["B"])
@@ -94,21 +98,46 @@ def test_workload_parity(name):
     assert err(fin, fr) <= tol_for(w.dtype)
 
 
-def test_long_context_parity_sampled_heads():
-    """128K tokens, 512 chunks: every output of sampled heads over the whole sequence,
-    including the heads with the slowest and the fastest decay."""
+def _err_bf16_by_head(got, ref, head_axis):
+    """The bf16 metric over a whole tensor, max |got - ref| / max |ref|, accumulated one
+    head at a time (the full 128K-token tensors are 400 M elements)."""
+    num = den = 0.0
+    for h in range(ref.shape[head_axis]):
+        r = np.take(ref, h, axis=head_axis)
+        gh = as_np(got.select(head_axis, h))
+        num = max(num, float(np.abs(gh - r).max()))
+        den = max(den, float(np.abs(r).max()))
+    return num / (den if den > 0 else 1.0)
+
+
+@pytest.fixture(scope="module")
+def long_context():
+    """Inputs of the 128K-token layer and the fp64 recurrence over all of it (computed once
+    for the tests below)."""
     w = WORKLOADS["long_context_b1_L131072_h48"]
     d = inputs.make(w)
-    y, fin = run_gpu(d, w.chunk)
-    A = d["A"].numpy()
-    heads = sorted({int(np.argmax(A)), int(np.argmin(A)), 0, 29})
-    sub = dict(x=d["x"][:, :, heads], dt=d["dt"][:, :, heads], A=d["A"][heads], B=d["B"],
-               C=d["C"], D=d["D"][heads], init_state=None)
-    yr, fr = oracle_layer(sub)
-    ys = y[:, :, heads]
-    assert err_bf16(ys, yr) <= 2e-2
-    assert err_bf16(fin[:, heads], fr) <= 2e-2
-    assert torch.isfinite(y.float()).all()
+    yr, fr = oracle_layer(d)
+    return w, d, yr, fr
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("Q", [256, 128, 64])
+def test_long_context_parity_every_head(long_context, Q):
+    """128K tokens, 48 heads: every output and every final-state element against the fp64
+    recurrence over the whole sequence, at the workload's Q = 256 (512 chunks) and at
+    Q = 128 and 64 (1024 and 2048 chunks).  For Q < 256 a chunk's decay rows are less than
+    one wave of 16-byte pieces, and the per-lane guard on their DMA keeps every read inside
+    the workspace (whose end coincides with the allocation's at this size)."""
+    w, d, yr, fr = long_context
+    y, fin = run_gpu(d, Q)
+    ycpu = y.cpu()
+    del y
+    e_y = _err_bf16_by_head(ycpu, yr, 2)
+    e_f = err_bf16(fin, fr)
+    print("long context Q=%d: y err %.3g, final_state err %.3g" % (Q, e_y, e_f))
+    assert e_y <= 2e-2
+    assert e_f <= 2e-2
+    assert torch.isfinite(ycpu.float()).all()
 
 
 @pytest.mark.parametrize("case", range(12))
@@ -197,24 +226,6 @@ def test_narrow_dt_variant():
     yr, fr = oracle_layer(d)
     assert err_bf16(y, yr) <= 2e-2
     assert err_bf16(fin, fr) <= 2e-2
-
-
-@pytest.mark.parametrize("Q", [64, 128])
-def test_long_context_smaller_chunks(Q):
-    """The 128K-token layer with Q = 64 and 128 (2048 and 1024 chunks): sampled heads over
-    the whole sequence.  For Q < 256 a chunk's decay rows are less than one wave of 16-byte
-    pieces, and the per-lane guard on their DMA keeps every read inside the workspace
-    (whose end coincides with the allocation's at this size)."""
-    w = WORKLOADS["long_context_b1_L131072_h48"]
-    d = inputs.make(w)
-    y, fin = run_gpu(d, Q)
-    A = d["A"].numpy()
-    heads = sorted({int(np.argmax(A)), int(np.argmin(A)), 7})
-    sub = dict(x=d["x"][:, :, heads], dt=d["dt"][:, :, heads], A=d["A"][heads], B=d["B"],
-               C=d["C"], D=d["D"][heads], init_state=None)
-    yr, fr = oracle_layer(sub)
-    assert err_bf16(y[:, :, heads], yr) <= 2e-2
-    assert err_bf16(fin[:, heads], fr) <= 2e-2
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

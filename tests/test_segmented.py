@@ -107,9 +107,12 @@ def test_swapped_layer_states_change_the_output():
     assert not torch.equal(y, y_sw)
 
 
+@pytest.mark.slow
 def test_vertical_stack_workload():
-    """24 layers, 32768 tokens, V = 2048: segmented == horizontal bit for bit; the oracle
-    checks every head on the first two segments and one head over the whole sequence."""
+    """24 layers, 32768 tokens, V = 2048: both segmented schedules equal the horizontal
+    order bit for bit, and the whole stack output (every segment, every head) and every
+    layer's final state are within tolerance of the fp64 stack oracle over the full
+    sequence."""
     w = WORKLOADS["vertical_stack_24x_L32768_V2048"]
     d = inputs.make(w)
     g = to_dev(d, DEV)
@@ -125,15 +128,12 @@ def test_vertical_stack_workload():
     torch.cuda.synchronize()
     assert torch.equal(y_seg, y_hor) and torch.equal(y_one, y_hor)
     assert torch.equal(s_seg, s_hor) and torch.equal(s_one, s_hor)
-    T = 2 * w.segment
-    yr, _ = oracle.stack_horizontal(d["x0"][:, :T], d["dt"][:, :T], d["A"], d["B"][:, :T], d["C"][:, :T],
-                                    d["D"])
-    assert err_bf16(y_seg[:, :T], yr) <= 2e-2
-    h = int(np.argmax(d["A"][0].numpy()))
-    yr1, fr1 = oracle.stack_horizontal(d["x0"][:, :, [h]], d["dt"][:, :, [h]], d["A"][:, [h]], d["B"],
-                                       d["C"], d["D"][:, [h]])
-    assert err_bf16(y_seg[:, :, [h]], yr1) <= 2e-2
-    assert err_bf16(s_seg[:, :, [h]], fr1) <= 2e-2
+    yr, fr = oracle.stack_horizontal(d["x0"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    e_y = err_bf16(y_seg, yr)
+    e_s = [err_bf16(s_seg[l], fr[l]) for l in range(nl)]
+    print("24-layer stack: y err %.3g, layer state err max %.3g" % (e_y, max(e_s)))
+    assert e_y <= 2e-2
+    assert max(e_s) <= 2e-2
 
 
 def test_wavefront_chunk_length_32_and_groups():
