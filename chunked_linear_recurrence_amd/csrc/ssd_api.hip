@@ -13,6 +13,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "ssd_common.h"
@@ -227,6 +228,40 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     return st == SSD_OK ? ok() : st;
 }
 
+// Scratch of ssd_chunk_scan_fwd_noalloc: the layer workspace lives in this file-scope
+// device array instead of caller memory.  Each GPU the library runs on holds its own copy
+// (SSD_NOALLOC_SCRATCH_BYTES) from module load until the process ends.  In host code the
+// array's name is only a stand-in: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device (scratch_on_current_device) and used for
+// every kernel argument.  Nothing in the workspace needs to start at zero (every stage
+// writes what the next one reads), so nothing is cleared between calls.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The address of this GPU's scratch array (the device current on the calling thread).
+ssd_status_t scratch_on_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SSD_ERR_UNSUPPORTED, "device index %d is beyond the %d devices the scratch table covers",
+                    dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(SSD_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +292,25 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, const void *x, const voi
                                 void *workspace, size_t workspace_bytes, void *stream) {
     return fwd_impl(dims, x, dt, A, B, C, D, init_state, chunk_Q, y, final_state, flags, workspace,
                     workspace_bytes, stream, 1, kStages);
+}
+
+ssd_status_t ssd_chunk_scan_fwd_noalloc(const ssd_dims_t *dims, const void *x, const void *dt, const float *A,
+                                        const void *B, const void *C, const float *D, const float *init_state,
+                                        int32_t chunk_Q, void *y, float *final_state, uint32_t flags,
+                                        void *stream) {
+    // The size check runs before anything touches the device.
+    ssd_status_t st = check_dims(dims, chunk_Q);
+    if (st != SSD_OK) return st;
+    Layout lo;
+    if (!layout_for(*dims, dims->seqlen, chunk_Q, &lo)) return fail(SSD_ERR_BAD_SHAPE, "sizes overflow");
+    if (lo.total > (size_t)SSD_NOALLOC_SCRATCH_BYTES)
+        return fail(SSD_ERR_WORKSPACE, "this call needs %zu bytes of workspace; the no-allocation entry "
+                    "point has %zu (use ssd_chunk_scan_fwd with a caller workspace)", lo.total,
+                    (size_t)SSD_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = scratch_on_current_device(&ws)) != SSD_OK) return st;
+    return fwd_impl(dims, x, dt, A, B, C, D, init_state, chunk_Q, y, final_state, flags, ws,
+                    (size_t)SSD_NOALLOC_SCRATCH_BYTES, stream, 1, kStages);
 }
 
 ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const void *dt, const float *A,

@@ -25,7 +25,10 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ER
 EXPORTS = ["ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_segmented_workspace_bytes",
            "ssd_chunk_scan_segmented", "ssd_chunk_scan_stages", "ssd_workspace_layout",
            "ssd_shape_supported", "ssd_status_string", "ssd_last_error_message", "ssd_version", "ssd_step",
-           "ssd_scan_form_supported"]
+           "ssd_scan_form_supported", "ssd_chunk_scan_fwd_noalloc"]
+
+# Workspace limit of ssd_chunk_scan_fwd_noalloc (SSD_NOALLOC_SCRATCH_BYTES in the header).
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 class Dims(ctypes.Structure):
@@ -57,6 +60,8 @@ def lib():
         L.ssd_chunk_scan_workspace_bytes.restype = sz
         L.ssd_chunk_scan_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp]
         L.ssd_chunk_scan_fwd.restype = ctypes.c_int
+        L.ssd_chunk_scan_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, u32, vp]
+        L.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
         L.ssd_chunk_scan_stages.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, u32, vp, sz, vp, i32, i32]
         L.ssd_chunk_scan_stages.restype = ctypes.c_int
         L.ssd_segmented_workspace_bytes.argtypes = [dp, i32, i64, i32, u32]
@@ -254,6 +259,22 @@ def fwd(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y=None, final_sta
         _check(lib().ssd_chunk_scan_fwd(*args))
     else:
         _check(lib().ssd_chunk_scan_stages(*args, first_stage, last_stage))
+    return y, final_state
+
+
+def fwd_noalloc(x, dt, A, B, C, D=None, init_state=None, chunk=256, *, y, final_state=None,
+                residual=False, stream=None):
+    """ssd_chunk_scan_fwd_noalloc: one layer with the library's own scratch as workspace
+    (nothing is allocated; y and final_state are caller tensors).  The workspace this call
+    needs (workspace_bytes) must not exceed NOALLOC_SCRATCH_BYTES.  Calls that overlap on
+    one GPU share that scratch and must be serialised by the caller.  Returns (y, final_state)."""
+    lib()                  # fails loudly when the library is not built
+    check_layer_args(x, dt, A, B, C, D, init_state, y, final_state)
+    dims = dims_of(x, B)
+    flags = SSD_FLAG_RESIDUAL if residual else 0
+    _check(lib().ssd_chunk_scan_fwd_noalloc(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                            _ptr(D), _ptr(init_state), chunk, _ptr(y), _ptr(final_state),
+                                            flags, _stream(stream)))
     return y, final_state
 
 

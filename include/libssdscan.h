@@ -142,6 +142,27 @@ ssd_status_t ssd_chunk_scan_fwd(const ssd_dims_t *dims, const void *x, const voi
                                 void *y, float *final_state, uint32_t flags,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* ssd_chunk_scan_fwd for callers that cannot allocate or pass device memory for a
+ * workspace (code under HIP graph capture that must not allocate, tight serving loops,
+ * harnesses that forbid allocation): the same computation, the same kernels and
+ * bit-identical results, with the workspace taken from a scratch array inside the
+ * library instead of a caller buffer.  Nothing is allocated or freed here.
+ *   Arguments as for ssd_chunk_scan_fwd, without workspace and workspace_bytes.
+ *   Limit: the workspace ssd_chunk_scan_workspace_bytes reports for these dims and chunk_Q
+ *   must not exceed SSD_NOALLOC_SCRATCH_BYTES (64 MiB; for example up to ~41K tokens of
+ *   batch * seqlen at nheads 24, headdim 64, dstate 128, chunk_Q 256, bf16); larger calls
+ *   return SSD_ERR_WORKSPACE before anything is enqueued.
+ *   Each GPU the library runs on holds one such array from the library's load until the
+ *   process ends, shared by every call on that GPU: calls that overlap on one GPU (on
+ *   different streams, or from several threads) race on it and must be serialised by
+ *   the caller.  The first call on a device resolves the array's address there.
+ * Returns SSD_OK once the kernels are enqueued on `stream`. */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+ssd_status_t ssd_chunk_scan_fwd_noalloc(const ssd_dims_t *dims, const void *x, const void *dt,
+                                        const float *A, const void *B, const void *C,
+                                        const float *D, const float *init_state, int32_t chunk_Q,
+                                        void *y, float *final_state, uint32_t flags, void *stream);
+
 /* Workspace size for ssd_chunk_scan_segmented with these n_layers and flags (0 when the
  * arguments are invalid).  Without SSD_FLAG_WAVEFRONT it is two segment buffers and one
  * layer workspace over V tokens; with it, depth = min(ceil(seqlen / V), n_layers) times

@@ -76,6 +76,28 @@ def test_fwd_argument_errors():
     assert _fwd(_dims(), init=FAKE + 2 ** 36, fin=FAKE + 2 ** 36 + 16) == 8
 
 
+def test_noalloc_rejects_workspaces_beyond_its_scratch():
+    """ssd_chunk_scan_fwd_noalloc checks the workspace it would need against its fixed
+    scratch before touching any device: too large a call fails with SSD_ERR_WORKSPACE,
+    and shape errors keep their own codes."""
+    L = _lib()
+    v = ctypes.c_void_p
+
+    def call(dims, Q=256):
+        return L.ssd_chunk_scan_fwd_noalloc(ctypes.byref(dims), v(FAKE), v(FAKE + 2 ** 30), v(FAKE + 2 ** 31),
+                                            v(FAKE + 2 ** 32), v(FAKE + 2 ** 33), None, None, Q,
+                                            v(FAKE + 2 ** 34), None, 0, None)
+    big = _dims(b=8, L=4096, H=32, P=64, N=128, dtype=1)       # 138 MB of workspace
+    assert L.ssd_chunk_scan_workspace_bytes(ctypes.byref(big), 256) > ssd.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 6
+    assert "64" in L.ssd_last_error_message().decode() or "67108864" in L.ssd_last_error_message().decode()
+    assert call(_dims(L=0)) == 2
+    assert call(_dims(dtype=1, N=16), Q=256) == 4
+    text = open(HEADER).read()
+    assert "#define SSD_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)" in text
+    assert ssd.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
+
+
 def test_segmented_argument_errors():
     L = _lib()
     d = _dims(L=512)
