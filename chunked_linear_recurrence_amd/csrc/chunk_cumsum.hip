@@ -1,19 +1,26 @@
 // chunk_cumsum: per chunk and head, the inclusive prefix sum of dt * A over the chunk's
-// tokens.  exp of entry i is the decay weight L_i of diag(L) in [分块推理 §2.2] (page
-// "分块推理：解锁循环模型并行计算，实现长序列高效处理"), exp of the last entry is the chunk's
-// total decay (the product of A_t over the chunk), and exp of differences gives every
-// intra-chunk decay.
+// tokens.  2^(entry i) is the decay weight L_i of diag(L) in [分块推理 §2.2] (page
+// "分块推理：解锁循环模型并行计算，实现长序列高效处理"), 2^(last entry) is the chunk's total
+// decay (the product of A_t over the chunk), and 2^(differences) give every intra-chunk
+// decay.  The sums are in base 2 (dt * A / ln 2): every consumer takes them through one
+// hardware 2^x.
 //
-// Layout: dA_cum[b, h, c, i], i < Q.  Positions past a short last chunk hold the chunk
-// total, so later kernels can read any index without special cases.  The totals are also
-// written contiguously, ctot[b, h, c], for the state pass.
+// Outputs, per (batch, head, chunk):
+//   dA_cum[b, h, c, i], i < Q   the prefix sums; positions past a short last chunk hold
+//                               the chunk total, so later kernels can read any index;
+//   ctot[b, h, c]               each chunk's total, contiguous, for the state pass;
+//   dblk[b, h, c, i]            2^(dA_cum[e(i)] - dA_cum[i]) with e(i) the last token of
+//                               i's 16-token block: the decay from token i to its block's
+//                               end (float32, <= 1).  chunk_scan factors every decay
+//                               between two tokens of different blocks through it.
 // Sums are float64 for float32 activations (dt * A is then exact) and float32 for
 // bfloat16 activations.
 //
 // Work: one workgroup per (batch, chunk, block of kCumHeads heads), one wave per head.  The
 // Q x kCumHeads tile of dt * A is staged in LDS with coalesced loads; each wave then scans
-// its head: every lane sums Q/64 consecutive values, and a 6-step wave shuffle scan
-// combines the lane totals.  HBM-bound (reads dt once, writes 4 bytes per token-head).
+// its head: every lane sums its Q/64 consecutive values (one vector read), and a 6-step
+// wave shuffle scan combines the lane totals.  HBM-bound (reads dt once, writes 8 or 12
+// bytes per token-head).
 #include "ssd_common.h"
 
 namespace ssd {
@@ -23,7 +30,7 @@ namespace ssd {
 // heads x 4 waves with four scans per wave, or whole 64-head token rows).
 constexpr int kCumHeads = 8, kCumThreads = kCumHeads * 64;
 
-// A lane's E consecutive values as one vector store (E * sizeof(V) bytes).
+// A lane's E consecutive values as one vector access (E * sizeof(V) bytes).
 template <typename V, int E>
 __device__ __forceinline__ void store_run(V *dst, const V (&v)[E]) {
     if constexpr (E * sizeof(V) % 16 == 0) {
@@ -42,14 +49,37 @@ __device__ __forceinline__ void store_run(V *dst, const V (&v)[E]) {
         for (int e = 0; e < E; ++e) dst[e] = v[e];
     }
 }
+template <typename V, int E>
+__device__ __forceinline__ void load_run(const V *src, V (&v)[E]) {
+    if constexpr (E * sizeof(V) % 16 == 0) {
+#pragma unroll
+        for (int k = 0; k < E * (int)sizeof(V) / 16; ++k) {
+            const uint4 u = reinterpret_cast<const uint4 *>(src)[k];
+            __builtin_memcpy(reinterpret_cast<unsigned char *>(v) + 16 * k, &u, 16);
+        }
+    } else if constexpr (E * sizeof(V) == 8) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(src);
+        __builtin_memcpy(v, &u, 8);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = src[e];
+    }
+}
+
+// Row pitch of the LDS tile (elements): 16 bytes of padding keeps every row 16-byte aligned
+// for the vector reads and puts the 8 heads' rows of one token on different banks for the
+// staging writes.
+template <typename S, int Q>
+constexpr int cum_pitch() { return Q + 16 / (int)sizeof(S); }
 
 template <typename T, int Q>
 __global__ __launch_bounds__(kCumThreads) void chunk_cumsum_kernel(Problem p0) {
     typedef typename CumT<T>::type S;
     constexpr int E = Q >= 64 ? Q / 64 : 1;      // values per lane
     constexpr int NA = Q / E;                    // lanes holding tokens (64, or Q when Q < 64)
+    constexpr int RP = cum_pitch<S, Q>();
     static_assert(16 % E == 0 && NA <= 64, "a lane's tokens lie in one 16-token block");
-    __shared__ S tile[kCumHeads][Q + 1];
+    __shared__ __align__(16) S tile[kCumHeads * RP];
     const int c = blockIdx.x, hb = blockIdx.y * kCumHeads, b = blockIdx.z % p0.batch;
     const Problem p = step_problem(p0, blockIdx.z / p0.batch);
     if (c >= p.nc) return;                       // past a short last segment (uniform)
@@ -58,11 +88,32 @@ __global__ __launch_bounds__(kCumThreads) void chunk_cumsum_kernel(Problem p0) {
     const T *dt = reinterpret_cast<const T *>(p.dt) + (int64_t)b * p.dt_bs;
     const int nh = min(kCumHeads, p.H - hb);
 
-    for (int idx = threadIdx.x; idx < Q * kCumHeads; idx += kCumThreads) {
-        const int j = idx / kCumHeads, hh = idx % kCumHeads;
-        S v = 0;
-        if (hh < nh && j < Qc) v = (S)to_f32(dt[(int64_t)(t0 + j) * p.H + hb + hh]) * (S)p.A[hb + hh];
-        tile[hh][j] = v;
+    // Stage dt * A / ln 2 for the block's heads, tile[hh][j].  When the block's 8 heads of a
+    // token are one aligned 16-byte run (bf16, all 8 heads present, H a multiple of 8), a
+    // thread loads a token's run at once; otherwise element by element.
+    const T *dtb = dt + (int64_t)t0 * p.H + hb;
+    if (sizeof(T) == 2 && nh == kCumHeads && p.H % 8 == 0 &&
+        (reinterpret_cast<uintptr_t>(dtb) & 15) == 0) {
+        for (int j = threadIdx.x; j < Q; j += kCumThreads) {
+            S a[kCumHeads];
+            if (j < Qc) {
+                const bf16x8 v = *reinterpret_cast<const bf16x8 *>(dtb + (int64_t)j * p.H);
+#pragma unroll
+                for (int hh = 0; hh < kCumHeads; ++hh) a[hh] = (S)to_f32(v[hh]);
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < kCumHeads; ++hh) a[hh] = 0;
+            }
+#pragma unroll
+            for (int hh = 0; hh < kCumHeads; ++hh) tile[hh * RP + j] = a[hh] * (S)((S)p.A[hb + hh] * (S)kLog2e);
+        }
+    } else {
+        for (int idx = threadIdx.x; idx < Q * kCumHeads; idx += kCumThreads) {
+            const int j = idx / kCumHeads, hh = idx % kCumHeads;
+            S v = 0;
+            if (hh < nh && j < Qc) v = (S)to_f32(dtb[(int64_t)j * p.H + hh]) * (S)((S)p.A[hb + hh] * (S)kLog2e);
+            tile[hh * RP + j] = v;
+        }
     }
     __syncthreads();
 
@@ -70,10 +121,14 @@ __global__ __launch_bounds__(kCumThreads) void chunk_cumsum_kernel(Problem p0) {
     const bool active = lane < NA;
     for (int hh = wave; hh < nh; hh += kCumThreads / 64) {
         S v[E];
+        if (active) load_run<S, E>(tile + hh * RP + lane * E, v);
+        else
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = 0;
         S run = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            if (active) run += tile[hh][lane * E + e];
+            run += v[e];
             v[e] = run;
         }
         // inclusive scan of the lane totals across the wave
@@ -87,7 +142,8 @@ __global__ __launch_bounds__(kCumThreads) void chunk_cumsum_kernel(Problem p0) {
         // a run of zero inputs past a short chunk repeats the chunk total exactly
         S excl = __shfl_up(incl, 1, 64);
         if (lane == 0) excl = 0;
-        S *out = reinterpret_cast<S *>(p.dA_cum) + (((int64_t)b * p.H + hb + hh) * p.nc + c) * Q + lane * E;
+        const int64_t row = (((int64_t)b * p.H + hb + hh) * p.nc + c) * Q;
+        S *out = reinterpret_cast<S *>(p.dA_cum) + row + lane * E;
         // value at the chunk's last token, broadcast to the padded positions
         const int last = Qc - 1;
         S lastv = excl + v[0];
@@ -98,7 +154,15 @@ __global__ __launch_bounds__(kCumThreads) void chunk_cumsum_kernel(Problem p0) {
         S cv[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) cv[e] = (lane * E + e <= last) ? excl + v[e] : lastv;
-        if (active) store_run<S, E>(out, cv);
+        // the value at the end of this lane's 16-token block (its last lane's last value)
+        const S bend = __shfl(cv[E - 1], ((lane * E) | 15) / E, 64);
+        float dl[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) dl[e] = exp2_fast((float)(bend - cv[e]));
+        if (active) {
+            store_run<S, E>(out, cv);
+            store_run<float, E>(p.dblk + row + lane * E, dl);
+        }
         if (lane == 0)                               // the chunk's total, for the state pass
             reinterpret_cast<S *>(p.ctot)[((int64_t)b * p.H + hb + hh) * p.nc + c] = lastv;
     }

@@ -23,44 +23,26 @@
 // never per head.
 //
 // Per head, x is brought into LDS by DMA (tokens x channels, read back as transposed
-// fragments), b_in likewise, and the chunk's log-decay prefix sums cum.  The products are
+// fragments), b_in likewise, and the chunk's log-decay prefix sums cum and block decays
+// dblk.  The products are
 // computed transposed (y^T[p][i]) so that a lane's 4 accumulator values are 4 consecutive
 // channels of one token:
-//     Z^T = b(c-1) C^T, column i scaled by G_i = exp(cum_i);
-//     y^T += x^T (S^T . decay), the decay of tile entry (j, i) being exp(cum_i - cum_j):
-//       <= 1 below the diagonal (cum is non-increasing), and exp(min(cum_i - cum_j, 0)) on
-//       diagonal tiles (the zeroed upper triangle of S^T does the masking); a lane's 4 S^T
-//       values are 4 consecutive k values of the B operand, so no data moves between
-//       lanes;
+//     Z^T = b(c-1) C^T, column i scaled by G_i = 2^(cum_i);
+//     y^T += x^T (S^T . decay), the decay of tile entry (j, i) being 2^(cum_i - cum_j)
+//       (cum holds base-2 sums of dt A).  Below the diagonal (token j in an earlier 16-token
+//       block J than i) it is factored through the end e_J of j's block:
+//         2^(cum_i - cum_j) = 2^(cum_i - cum_{e_J}) * dblk_j,   dblk_j = 2^(cum_{e_J} - cum_j),
+//       both factors <= 1 (cum is non-increasing), dblk precomputed per token by
+//       chunk_cumsum: one 2^x per tile and lane instead of one per entry.  On diagonal
+//       tiles it is 2^(min(cum_i - cum_j, 0)) per entry (the zeroed upper triangle of S^T
+//       does the masking).  A lane's 4 S^T values are 4 consecutive k values of the B
+//       operand (and share one column i), so no data moves between lanes;
 //     y^T += x^T diag(D + residual) on the matrix cores (D split in a high and a low bf16
 //       part so the skip term keeps fp32 accuracy; K = 16 products).
 // Tiles are paired into 16x16x32 bf16 products (16x16x4 f32 for the fp32 dtype).
-#include "ssd_common.h"
+#include "ssd_index.h"
 
 namespace ssd {
-
-template <typename T, int Q, int P, int N>
-struct ScanCfg {
-    static constexpr int NRB = Q / 16, NW = NRB / 2, THREADS = NW * 64;
-    static constexpr int NSLOT = NRB + 2, NPAIR = NSLOT / 2;
-    static constexpr int NTRI = NRB * (NRB + 1) / 2;            // causal tiles per chunk
-    static constexpr int PT = P / 16, NT = N / 16;
-    // one head's inputs in LDS: x tile, b(c-1) tile, cum row (the layout of HeadBuf)
-    static constexpr int HEAD_BYTES = Q * P * (int)sizeof(T) + P * N * (int)sizeof(T) +
-                                      Q * (int)sizeof(typename CumT<T>::type);
-    static constexpr bool DB = 2 * HEAD_BYTES <= kLdsBytes;     // double-buffered head data
-    static constexpr int YPIECES = P * (int)sizeof(T) / 16;      // 16-byte pieces per output row
-    static constexpr int YW = 32 * P * (int)sizeof(T);           // one wave's staged outputs
-    static constexpr bool YS = DB && 2 * HEAD_BYTES + NW * YW <= kLdsBytes;
-    static constexpr int LDS = (DB ? 2 * HEAD_BYTES : HEAD_BYTES) + (YS ? NW * YW : 0);
-    // The chunk's B tile (Q x N) is staged in LDS for the S^T products when it fits beside
-    // the first head's buffer; otherwise the B fragments are loaded from L2.
-    static constexpr int BPIECES = N * (int)sizeof(T) / 16;      // 16-byte pieces per B row
-    static constexpr bool BL = DB && Q * N * (int)sizeof(T) <= LDS - HEAD_BYTES;
-    static constexpr bool OK = LDS <= kLdsBytes &&
-                               (sizeof(T) == 4 || NT % 2 == 0) && (Q == 32 || Q == 64 || Q == 128 || Q == 256) &&
-                               P * (int)sizeof(T) >= 32;
-};
 
 // Slot s of wave w: row block, column block, pad flag (all uniform).
 struct Slot {
@@ -91,11 +73,19 @@ __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, kCachePolicyNT);
 }
 
-// x tile in LDS: row-major [Q][P] in 16-byte pieces; piece q of row r is stored at
-// position q ^ swz(r) of that row, which spreads the 4 rows read by one transpose load
-// over different banks.
-template <int PIECES>
-__device__ __forceinline__ int x_swz(int r) { return (((r >> 1) & 3) << 1) & (PIECES - 1); }
+// The per-head copies and stores go through buffer descriptors: a uniform base in scalar
+// registers (rebuilt per head with scalar arithmetic) and a 32-bit per-lane offset, so a
+// lane's address costs one vector register instead of two.  Offsets at or past `bytes`
+// read zeros and drop stores (a bound on top of the kernel's own guards).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferWord3 = 0x00020000;     // untyped buffer, 32-bit data format (gfx9 family)
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ void dma16_buf(rsrc_t r, uint32_t voff, void *lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, voff, 0, 0, kCachePolicyNT);
+}
+
 
 // A operand fragment of x^T for (16-token block J, 16-channel tile pt): lane (col, g) gets
 // x[16J + 4g + e][16pt + col], e = 0..3.
@@ -108,7 +98,7 @@ __device__ __forceinline__ bf16x4 x_frag<bf16, 16>(const unsigned char *xs, int 
     const int s = lane & 15, g = lane >> 4;
     const int r = J * 16 + 4 * g + (s >> 2);
     const int c = pt * 16 + 4 * (s & 3);
-    const int q = (c >> 3) ^ x_swz<PIECES>(r);
+    const int q = (c >> 3) ^ x_swz(r, PIECES);
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(xs + r * (P * 2) + q * 16 + (c & 7) * 2));
 }
 #define SSD_XFRAG_BF16(PP)                                                                           \
@@ -118,7 +108,7 @@ __device__ __forceinline__ bf16x4 x_frag<bf16, 16>(const unsigned char *xs, int 
         const int s = lane & 15, g = lane >> 4;                                                      \
         const int r = J * 16 + 4 * g + (s >> 2);                                                     \
         const int c = pt * 16 + 4 * (s & 3);                                                         \
-        const int q = (c >> 3) ^ x_swz<PIECES>(r);                                                   \
+        const int q = (c >> 3) ^ x_swz(r, PIECES);                                                   \
         return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(xs + r * (PP * 2) + q * 16 + (c & 7) * 2)); \
     }
 SSD_XFRAG_BF16(32)
@@ -142,16 +132,6 @@ SSD_XFRAG_F32(64)
 SSD_XFRAG_F32(128)
 #undef SSD_XFRAG_F32
 
-template <typename T, int Q, int P, int N>
-struct HeadBuf {
-    typedef typename CumT<T>::type S;
-    static constexpr int X = Q * P * (int)sizeof(T);
-    static constexpr int ST = P * N * (int)sizeof(T);
-    static constexpr int CM = Q * (int)sizeof(S);
-    static constexpr int O_ST = X, O_CM = X + ST;
-    static constexpr int BYTES = O_CM + CM;
-};
-
 // Per-head products of wave W (all slot choices and offsets are compile-time):
 // Z^T scaled by G, the decayed S^T tiles times x^T, and (D + res) x.  hook(k, nbuf, ys)
 // is called at 1 + PT + NPAIR fixed points of the body (k known at compile time once
@@ -167,7 +147,6 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
                                       float dres, int lane, f32x4 (&acc)[2][ScanCfg<T, Q, P, N>::PT],
                                       Hook &&hook) {
     using Cfg = ScanCfg<T, Q, P, N>;
-    using Buf = HeadBuf<T, Q, P, N>;
     using F = typename TF<T>::type;
     typedef typename CumT<T>::type S;
     constexpr int NRB = Cfg::NRB, PT = Cfg::PT, NT = Cfg::NT;
@@ -175,8 +154,9 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
     constexpr int w = W, I0 = W, I1 = NRB - 1 - W;
     const int col = lane & 15, g4 = 4 * (lane >> 4);
     const unsigned char *xs = buf;
-    const T *stb = reinterpret_cast<const T *>(buf + Buf::O_ST);
-    const S *cm = reinterpret_cast<const S *>(buf + Buf::O_CM);
+    const T *stb = reinterpret_cast<const T *>(buf + Cfg::O_ST);
+    const S *cm = reinterpret_cast<const S *>(buf + Cfg::O_CM);
+    const float *dlk = reinterpret_cast<const float *>(buf + Cfg::O_DL);
 
     // Output tiles are transposed: acc[ri][pt] lane (col, g), value r holds
     // y^T[p = pt*16 + 4g + r][i = I*16 + col].
@@ -205,7 +185,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
     }
     const S ci0 = cm[I0 * 16 + col], ci1 = cm[I1 * 16 + col];
     {
-        const float gi0 = __expf((float)ci0), gi1 = __expf((float)ci1);
+        const float gi0 = exp2_fast((float)ci0), gi1 = exp2_fast((float)ci1);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -227,14 +207,19 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
             const S ci = sl.first ? ci0 : ci1;
             Jx[u] = sl.J;
             f32x4 m;
-            if (sl.J < sl.I) {                              // uniform: off-diagonal tile or pad
-                // cum is non-increasing (dt A <= 0), so ci - cum_j <= 0 here
+            if (sl.pad) {                                   // uniform: the zero pad slot
+                m = zero_frag<f32x4>();
+            } else if (sl.J < sl.I) {                       // uniform: off-diagonal tile
+                // 2^(cum_i - cum_{e_J}) times dblk_j; cum is non-increasing (dt A <= 0), so
+                // both factors are <= 1
+                const float f = exp2_fast((float)(ci - cm[sl.J * 16 + 15]));
+                const f32x4 dl = *reinterpret_cast<const f32x4 *>(dlk + sl.J * 16 + g4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) m[r] = sT[s][r] * __expf((float)(ci - cm[sl.J * 16 + g4 + r]));
+                for (int r = 0; r < 4; ++r) m[r] = sT[s][r] * (f * dl[r]);
             } else {                                        // diagonal (masked in S^T)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    m[r] = sT[s][r] * __expf(fminf((float)(ci - cm[sl.J * 16 + g4 + r]), 0.f));
+                    m[r] = sT[s][r] * exp2_fast(fminf((float)(ci - cm[sl.J * 16 + g4 + r]), 0.f));
             }
             a[u] = frag_from_f32<T>(m);
         }
@@ -274,29 +259,18 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
     }
 }
 
-// Staged outputs of one wave: 32 rows (its two row blocks) of YPIECES 16-byte pieces;
-// piece q of row r sits at position q ^ ysw(r), so the fragment writes and the row reads
-// both spread over all banks.
-template <int YPIECES>
-__device__ __forceinline__ int ysw(int r) { return r & ((YPIECES < 8 ? YPIECES : 8) - 1); }
-
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_kernel(Problem p0) {
     const Problem p = step_problem(p0, blockIdx.y);
     using Cfg = ScanCfg<T, Q, P, N>;
-    using Buf = HeadBuf<T, Q, P, N>;
     using F = typename TF<T>::type;
     typedef typename CumT<T>::type S;
-    constexpr int THREADS = Cfg::THREADS, NW = Cfg::NW;
+    constexpr int NW = Cfg::NW;
     constexpr int NRB = Cfg::NRB, NSLOT = Cfg::NSLOT, PT = Cfg::PT, NT = Cfg::NT;
-    constexpr int XPIECES = P * (int)sizeof(T) / 16;          // 16-byte pieces per x row
-    constexpr int YPIECES = Cfg::YPIECES;
-    // memory work per head and wave, in single-instruction items:
-    constexpr int XK = (Q * XPIECES + THREADS - 1) / THREADS;           // x tile
-    constexpr int SP = Buf::ST / 16, SK = (SP + THREADS - 1) / THREADS;  // b_in state
-    constexpr int CP = Buf::CM / 16;                                     // cum
-    constexpr int NDMA = XK + SK + 1;
-    constexpr int NSTQ = 32 * YPIECES / 64;                               // staged-output stores
+    constexpr int XPIECES = Cfg::XPIECES, YPIECES = Cfg::YPIECES;
+    // memory work per head and wave, in single-instruction items (Cfg): XK x pieces, SK
+    // b_in pieces, one cum row, one dblk row, then NSTQ staged-output stores
+    constexpr int XK = Cfg::XK, SK = Cfg::SK, NDMA = Cfg::NDMA, NSTQ = Cfg::NSTQ;
     constexpr int NHOOK = 1 + PT + Cfg::NPAIR;
     constexpr int NITEM = NDMA + (Cfg::YS ? NSTQ : 0);
     static_assert(NSTQ * 64 == 32 * YPIECES, "output rows must fill whole store instructions");
@@ -325,58 +299,73 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
 
     const unsigned char *xchunk = reinterpret_cast<const unsigned char *>(p.x) +
                                   ((int64_t)b * p.x_bs + (int64_t)t0 * HP) * (int64_t)sizeof(T);
-    // DMA item k of head h into buffer buf: x pieces, then b_in pieces, then cum/F/G.
-    // Lane l of the wave fills LDS bytes [16 l, 16 l + 16) of the item's 1 KB block.
+    // Per-lane byte offsets of this lane's x pieces inside one head's slice of the chunk
+    // (the same for every head: the head only moves the uniform base), kept in 32 bits
+    // (the host bounds a chunk's span of x, Q * H * P * sizeof(T), below 2^31).
+    const uint32_t xrow = (uint32_t)(HP * (int)sizeof(T)), xhead = (uint32_t)(P * (int)sizeof(T));
+    uint32_t xoff[XK];
+#pragma unroll
+    for (int k = 0; k < XK; ++k) {
+        const DmaPiece d = scan_x_piece(k, w, lane, NW, Q, XPIECES, sizeof(T) == 2);
+        const int rr = min(d.row, Qc - 1);                      // rows past a short chunk repeat the last
+        xoff[k] = (uint32_t)rr * xrow + (uint32_t)(d.piece * 16);
+    }
+    // DMA item k of head h into buffer buf (indices from ssd_index.h): x pieces, then b_in
+    // pieces, then the cum row (waves from 0 up) and the dblk row (waves from NW - 1 down).
+    // Each source is one buffer covering exactly this (head, chunk)'s data.
     auto dma_item = [&](int k, int h, unsigned char *buf) {
         if (k < XK) {
-            const int piece = (k * NW + w) * 64 + lane;
-            if ((k * NW + w) * 64 < Q * XPIECES) {              // uniform (Q * XPIECES % 64 == 0)
-                const int r = piece / XPIECES, qp = piece % XPIECES;
-                const int q = qp ^ (sizeof(T) == 2 ? x_swz<XPIECES>(r) : 0);
-                const int rr = min(r, Qc - 1);                  // rows past a short chunk repeat the last
-                dma16(xchunk + ((int64_t)rr * HP + (int64_t)h * P) * (int64_t)sizeof(T) + q * 16,
-                      buf + (k * NW + w) * 1024);
-            }
+            const DmaPiece d = scan_x_piece(k, w, lane, NW, Q, XPIECES, sizeof(T) == 2);
+            if (d.on)                                           // uniform (whole waves of pieces)
+                dma16_buf(make_rsrc(xchunk + (int64_t)h * xhead, (uint32_t)(Qc - 1) * xrow + xhead), xoff[k],
+                          buf + d.lds - lane * 16);
         } else if (k < XK + SK) {
-            const int kk = k - XK;
-            if ((kk * NW + w) * 64 < SP) {
+            const DmaPiece d = scan_flat_piece(k - XK, w, lane, NW, Cfg::SP);
+            if (d.on) {
                 const unsigned char *sv = reinterpret_cast<const unsigned char *>(p.b_in) +
                                           (((int64_t)b * p.nc + c) * p.H + h) * PN * (int64_t)sizeof(T);
-                dma16(sv + ((kk * NW + w) * 64 + lane) * 16, buf + Buf::O_ST + (kk * NW + w) * 1024);
+                dma16_buf(make_rsrc(sv, Cfg::ST), (uint32_t)(d.piece * 16), buf + Cfg::O_ST + d.lds - lane * 16);
             }
         } else {
-            // cum of one (head, chunk) is CP 16-byte pieces, which need not fill whole
-            // waves (Q < 256 for bf16): the guard is per lane, so no lane reads past the row
-            // or writes past its LDS region
             const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
-            const int pc = w * 64 + lane;
-            // a per-wave test where the pieces fill whole waves (no exec-mask branch)
-            if ((CP % 64 == 0) ? (w * 64 < CP) : (pc < CP))
-                dma16(reinterpret_cast<const unsigned char *>(reinterpret_cast<const S *>(p.dA_cum) + tok) + pc * 16,
-                      buf + Buf::O_CM + w * 1024);
+            if (k == XK + SK) {                                 // cum row
+                const DmaPiece d = scan_row_piece(w, lane, Cfg::CP);
+                if (d.on)
+                    dma16_buf(make_rsrc(reinterpret_cast<const S *>(p.dA_cum) + tok, Cfg::CM),
+                              (uint32_t)(d.piece * 16), buf + Cfg::O_CM + d.lds - lane * 16);
+            } else {                                            // dblk row
+                const DmaPiece d = scan_row_piece(NW - 1 - w, lane, Cfg::DP);
+                if (d.on)
+                    dma16_buf(make_rsrc(p.dblk + tok, Cfg::DL), (uint32_t)(d.piece * 16),
+                              buf + Cfg::O_DL + d.lds - lane * 16);
+            }
         }
     };
-    static_assert(CP <= THREADS, "cum fits one DMA item");
-    static_assert(Buf::BYTES == Cfg::HEAD_BYTES, "head buffer layout and LDS sizing agree");
     // the x, state and B pieces always fill whole waves, so their guards are uniform
-    static_assert((Q * XPIECES) % 64 == 0 && SP % 64 == 0 && (Q * Cfg::BPIECES) % 64 == 0,
+    static_assert((Q * XPIECES) % 64 == 0 && Cfg::SP % 64 == 0 && (Q * Cfg::BPIECES) % 64 == 0,
                   "x, state and B tiles are whole waves of 16-byte pieces");
 
     T *ychunk = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)t0 * HP;
-    unsigned char *ys = smem + (Cfg::DB ? 2 : 1) * Buf::BYTES + (Cfg::YS ? w * Cfg::YW : 0);
+    unsigned char *ys = smem + (Cfg::DB ? 2 : 1) * Cfg::HEAD_BYTES + (Cfg::YS ? w * Cfg::YW : 0);
     // Store item k of head hs: 64 pieces of this wave's staged rows, 16 bytes per lane,
-    // whole output rows per group of YPIECES lanes.
+    // whole output rows per group of YPIECES lanes; per-lane byte offsets inside one head's
+    // slice of the chunk (32 bits, as for x).
+    uint32_t yoff[NSTQ];
+#pragma unroll
+    for (int k = 0; k < NSTQ; ++k) {
+        const DmaPiece d = scan_y_piece(k, lane, YPIECES);
+        const int i = (d.row < 16 ? I0 : I1) * 16 + (d.row & 15);
+        yoff[k] = (uint32_t)i * (uint32_t)(HP * (int)sizeof(T)) + (uint32_t)(d.piece * 16);
+    }
     auto store_item = [&](int k, int hs, const unsigned char *ys) {
-        const int pc = k * 64 + lane;
-        const int row = pc / YPIECES, q = pc % YPIECES;
-        const int i = (row < 16 ? I0 : I1) * 16 + (row & 15);
+        const DmaPiece d = scan_y_piece(k, lane, YPIECES);
+        const int i = (d.row < 16 ? I0 : I1) * 16 + (d.row & 15);
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + (row * YPIECES + (q ^ ysw<YPIECES>(row))) * 16);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + d.lds);
         // y is written once and not read again in this step: non-temporal.  Only the last
         // chunk can be short, so full chunks skip the per-lane row check.
-        u32x4 *dst = reinterpret_cast<u32x4 *>(ychunk + (int64_t)i * HP + (int64_t)hs * P + q * (16 / (int)sizeof(T)));
-        if (Qc == Q) __builtin_nontemporal_store(v, dst);
-        else if (i < Qc) __builtin_nontemporal_store(v, dst);
+        const rsrc_t r = make_rsrc(ychunk + (int64_t)hs * P, (uint32_t)(Qc - 1) * xrow + xhead);
+        if (Qc == Q || i < Qc) __builtin_amdgcn_raw_buffer_store_b128(v, r, yoff[k], 0, kCachePolicyNT);
     };
 
 #pragma unroll
@@ -406,8 +395,8 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         // B fragment of row j, columns n0..n0+3: from the staged tile (piece q of row j at
         // position q ^ bsw(j), so the 16 rows read by one load hit different banks) or
         // from L2.
-        constexpr int BMASK = (Cfg::BPIECES < 16 ? Cfg::BPIECES : 16) - 1;
-        const unsigned char *bst = smem + Buf::BYTES;
+        constexpr int BMASK = b_mask(Cfg::BPIECES);
+        const unsigned char *bst = smem + Cfg::HEAD_BYTES;
         auto bfrag = [&](int j, int n0) -> F {
             if (j >= Qc) return zero_frag<F>();
             if constexpr (Cfg::BL) {
@@ -421,15 +410,12 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         if constexpr (Cfg::BL) {
             // DMA the tile (rows past a short chunk repeat the last row; bfrag zeroes them)
             const unsigned char *bsrc = reinterpret_cast<const unsigned char *>(Bb);
-            constexpr int BK = (Q * Cfg::BPIECES + THREADS - 1) / THREADS;
 #pragma unroll
-            for (int k = 0; k < BK; ++k) {
-                if ((k * NW + w) * 64 < Q * Cfg::BPIECES) {     // uniform
-                    const int slot = (k * NW + w) * 64 + lane;
-                    const int j = slot / Cfg::BPIECES, q = (slot % Cfg::BPIECES) ^ (j & BMASK);
-                    dma16(bsrc + (int64_t)min(j, Qc - 1) * bcp * (int64_t)sizeof(T) + q * 16,
-                          smem + Buf::BYTES + (k * NW + w) * 1024);
-                }
+            for (int k = 0; k < Cfg::BK; ++k) {
+                const DmaPiece d = scan_b_piece(k, w, lane, NW, Q, Cfg::BPIECES);
+                if (d.on)                                       // uniform
+                    dma16(bsrc + (int64_t)min(d.row, Qc - 1) * bcp * (int64_t)sizeof(T) + d.piece * 16,
+                          smem + Cfg::HEAD_BYTES + d.lds - lane * 16);
             }
             __builtin_amdgcn_s_waitcnt(0);    // the tile (and the first head's inputs) landed
             __builtin_amdgcn_s_barrier();
@@ -465,8 +451,8 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
 
     const float res = (p.flags & 1u) ? 1.f : 0.f;
     for (int h = h0, it = 0; h < h1; ++h, ++it) {
-        unsigned char *buf = smem + (Cfg::DB ? (it & 1) * Buf::BYTES : 0);
-        unsigned char *nbuf = smem + (Cfg::DB ? ((it + 1) & 1) * Buf::BYTES : 0);
+        unsigned char *buf = smem + (Cfg::DB ? (it & 1) * Cfg::HEAD_BYTES : 0);
+        unsigned char *nbuf = smem + (Cfg::DB ? ((it + 1) & 1) * Cfg::HEAD_BYTES : 0);
         __builtin_amdgcn_s_waitcnt(0);        // this head's DMA (and older stores) complete
         __builtin_amdgcn_s_barrier();         // ... for every wave; the other buffer is free
         const bool more = h + 1 < h1;
@@ -497,9 +483,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
                 for (int pt = 0; pt < PT; ++pt) {
                     const int row = ri * 16 + col;
                     const int byte = (pt * 16 + g4) * (int)sizeof(T);
-                    const int q = (byte >> 4) ^ ysw<YPIECES>(row);
-                    *reinterpret_cast<F *>(ys + (row * YPIECES + q) * 16 + (byte & 15)) =
-                        frag_from_f32<T>(acc[ri][pt]);
+                    *reinterpret_cast<F *>(ys + scan_y_stage(row, byte, YPIECES)) = frag_from_f32<T>(acc[ri][pt]);
                 }
         } else {
             T *yh = ychunk + h * P;
@@ -542,14 +526,6 @@ static hipError_t launch_scan_t(const Problem &p, hipStream_t s) {
         return hipGetLastError();
     }
 }
-
-#define SSD_SCAN_SHAPES(X, T)                                                              \
-    X(T, 32, 32, 64) X(T, 32, 64, 64) X(T, 32, 64, 128)                                    \
-    X(T, 64, 16, 16) X(T, 64, 16, 32) X(T, 64, 16, 64) X(T, 64, 16, 128)                   \
-    X(T, 64, 32, 32) X(T, 64, 32, 64) X(T, 64, 32, 128) X(T, 64, 64, 64) X(T, 64, 64, 128) \
-    X(T, 128, 32, 64) X(T, 128, 64, 64) X(T, 128, 64, 128)                                 \
-    X(T, 256, 16, 32) X(T, 256, 32, 64) X(T, 256, 64, 64) X(T, 256, 64, 128)               \
-    X(T, 256, 128, 128) X(T, 256, 64, 256)
 
 #define SSD_SCAN_CASE(T, q, pp, nn) \
     if (p.Q == q && p.P == pp && p.N == nn) return launch_scan_t<T, q, pp, nn>(p, s);

@@ -12,12 +12,12 @@
 //     its 64 tokens in log2(64) = 6 cross-lane steps: spans 1, 2, 4, 8 inside each
 //     16-lane row (DPP row shifts), then the end of row r joined to row r + 1 and lane 31
 //     to rows 2-3 (DPP row broadcasts); every step multiplies the incoming partial value
-//     by the decay across the span it skips, exp(cum_t - cum_s) (per lane, computed once
+//     by the decay across the span it skips, 2^(cum_t - cum_s) (per lane, computed once
 //     from the chunk's dA_cum row);
 //   - lane 63 leaves its window's end value in LDS; the state entering window w is then
-//     exp(cum_{64w-1}) b_in + sum_{w' < w} exp(cum_{64w-1} - cum_{64w'+63}) end_{w'}
+//     2^(cum_{64w-1}) b_in + sum_{w' < w} 2^(cum_{64w-1} - cum_{64w'+63}) end_{w'}
 //     (the top levels of the tree, across the chunk's Q/64 windows), and reaches token t
-//     with the factor exp(cum_t - cum_{64w-1});
+//     with the factor 2^(cum_t - cum_{64w-1}) (cum: base-2 sums of dt A);
 //   - y_t[p] accumulates C_t[n] h_t[n] over n in a register.
 // y_t = sum_n C_t[n] h_t[n] + (D + residual) x_t, rounded once to the activation dtype.
 // B and C of the chunk are staged once in LDS with one padding word per row, so the 64
@@ -109,7 +109,7 @@ __global__ __launch_bounds__((AssocCfg<T, Q, P, N>::THREADS)) void chunk_scan_as
     const int tc = t < Q ? t : Q - 1;
     const S ct = cum[tc];
     const S cws = w > 0 ? cum[w * 64 - 1] : (S)0;             // sum before this window
-    const float Pw = __expf((float)(ct - cws));                // window start .. t
+    const float Pw = exp2_fast((float)(ct - cws));                // window start .. t
     // decays of the six tree steps: row shifts by d = 1, 2, 4, 8 (from lane t - d of the
     // same 16-lane row), then row ends (rows 1 and 3 take the end of the row before) and
     // lane 31 (rows 2 and 3); zero where the step adds nothing or the lane is past Q
@@ -118,14 +118,14 @@ __global__ __launch_bounds__((AssocCfg<T, Q, P, N>::THREADS)) void chunk_scan_as
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int d = 1 << s;
-        M[s] = (lr >= d && t < Q) ? __expf((float)(ct - cum[t - d >= 0 ? t - d : 0])) : 0.f;
+        M[s] = (lr >= d && t < Q) ? exp2_fast((float)(ct - cum[t - d >= 0 ? t - d : 0])) : 0.f;
     }
-    M[4] = ((row & 1) && t < Q) ? __expf((float)(ct - cum[min(w0 + 16 * row - 1, Q - 1)])) : 0.f;
-    M[5] = (row >= 2 && t < Q) ? __expf((float)(ct - cum[w0 + 31])) : 0.f;
-    const float Dwin = __expf((float)cws);                     // chunk start .. window start
+    M[4] = ((row & 1) && t < Q) ? exp2_fast((float)(ct - cum[min(w0 + 16 * row - 1, Q - 1)])) : 0.f;
+    M[5] = (row >= 2 && t < Q) ? exp2_fast((float)(ct - cum[w0 + 31])) : 0.f;
+    const float Dwin = exp2_fast((float)cws);                     // chunk start .. window start
     float Dww[NWIN];                                           // end of window w' .. window start
 #pragma unroll
-    for (int v = 0; v < NWIN; ++v) Dww[v] = v < w ? __expf((float)(cws - cum[min(v * 64 + 63, Q - 1)])) : 0.f;
+    for (int v = 0; v < NWIN; ++v) Dww[v] = v < w ? exp2_fast((float)(cws - cum[min(v * 64 + 63, Q - 1)])) : 0.f;
     const float dres = (p.D ? p.D[h] : 0.f) + ((p.flags & 1u) ? 1.f : 0.f);
     const T *xr = reinterpret_cast<const T *>(p.x) + (int64_t)b * p.x_bs + (int64_t)(t0 + (act ? t : 0)) * HP + h * P;
     T *yr = reinterpret_cast<T *>(p.y) + (int64_t)b * p.y_bs + (int64_t)(t0 + (act ? t : 0)) * HP + h * P;

@@ -1,9 +1,9 @@
 // chunk_state: every chunk's local end state from a zero initial state, b_intra(c) of
 // [分块推理 §2.1] (page "分块推理：解锁循环模型并行计算，实现长序列高效处理"):
 //
-//     b_intra(c)[p][n] = sum_j  exp(cum[last] - cum[j]) * x[j][p] * B[j][n]
+//     b_intra(c)[p][n] = sum_j  2^(cum[last] - cum[j]) * x[j][p] * B[j][n]
 //
-// over the chunk's tokens j, where cum is the chunk's dA_cum row.  Written as a matrix
+// over the chunk's tokens j, where cum is the chunk's dA_cum row (base-2 sums of dt A).  Written as a matrix
 // product it is  b_intra^T = B_c^T (N x Q) * (w . x_c) (Q x P)  with w_j the decay from
 // token j to the chunk end, a K = Q contraction on the matrix cores (bf16 in, fp32
 // accumulate; fp32 in for the fp32 dtype).
@@ -180,7 +180,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_k
                 const int jb = blk / (P / CW), pb = blk % (P / CW);
                 float w[RJ];
 #pragma unroll
-                for (int i = 0; i < RJ; ++i) w[i] = __expf((float)(clast - cw[k][i]));
+                for (int i = 0; i < RJ; ++i) w[i] = exp2_fast((float)(clast - cw[k][i]));
                 store_block_t<T, RJ, RS, true>(xw, jb * RJ, pb * CW, xr[k], w);
             }
         }

@@ -42,7 +42,7 @@ constexpr int kStages = 4;   // chunk_cumsum, chunk_state, state_pass, chunk_sca
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t dA, bintra, bin, ctot, total;
+    size_t dA, bintra, bin, ctot, dblk, total;
 };
 
 int64_t act_bytes(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
@@ -72,6 +72,9 @@ bool layout_for(const ssd_dims_t &d, int64_t L, int32_t Q, Layout *lo) {
     // each chunk's total log-decay, contiguous per (batch, head) for the state pass
     lo->ctot = off;
     off += align_up((size_t)bhn * (d.dtype == SSD_F32 ? 8 : 4));
+    // per token, the decay to the end of its 16-token block (float32), for chunk_scan
+    lo->dblk = off;
+    off += align_up((size_t)t * 4);
     lo->total = off;
     return true;
 }
@@ -93,6 +96,11 @@ ssd_status_t check_dims(const ssd_dims_t *d, int32_t Q) {
     if (d->seqlen > INT32_MAX || d->nheads > 65536 || d->batch > 65536 ||
         d->nheads * d->headdim > INT32_MAX / 16)
         return fail(SSD_ERR_UNSUPPORTED, "dimensions exceed the 32-bit index range of the kernels");
+    // the kernels address one chunk of x, y, B or C with 32-bit byte offsets
+    const int64_t e = act_bytes(d->dtype);
+    if ((int64_t)Q * d->nheads * d->headdim * e > INT32_MAX || (int64_t)Q * d->ngroups * d->dstate * e > INT32_MAX ||
+        d->headdim * d->dstate * e > INT32_MAX)
+        return fail(SSD_ERR_UNSUPPORTED, "one chunk of x or B, or one state, spans more than 2^31 bytes");
     if (!ssd_shape_supported(d->dtype, Q, d->headdim, d->dstate))
         return fail(SSD_ERR_UNSUPPORTED, "no compiled kernel for dtype %d chunk_Q %d headdim %lld dstate %lld",
                     d->dtype, Q, (long long)d->headdim, (long long)d->dstate);
@@ -222,6 +230,7 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     p.dA_cum = ws + lo.dA;
     p.ctot = ws + lo.ctot;
+    p.dblk = reinterpret_cast<float *>(ws + lo.dblk);
     p.b_intra = ws + lo.bintra;
     p.b_in = ws + lo.bin;
     st = run_layer(p, static_cast<hipStream_t>(stream), first_stage, last_stage);
@@ -429,6 +438,7 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
         q.lws_each = sl.lws_each;
         q.o_dA = sl.lo.dA;
         q.o_ctot = sl.lo.ctot;
+        q.o_dblk = sl.lo.dblk;
         q.o_bintra = sl.lo.bintra;
         q.o_bin = sl.lo.bin;
         q.dt0 = dt;
@@ -477,6 +487,7 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
                 p.flags = flags & SSD_FLAG_RESIDUAL;
                 p.dA_cum = lws + sl.lo.dA;
                 p.ctot = lws + sl.lo.ctot;
+                p.dblk = reinterpret_cast<float *>(lws + sl.lo.dblk);
                 p.b_intra = lws + sl.lo.bintra;
                 p.b_in = lws + sl.lo.bin;
                 st = run_layer(p, s, 1, kStages);

@@ -47,7 +47,7 @@ struct Steps {
     size_t act_each;
     unsigned char *lws;        // [depth] layer workspaces of lws_each bytes
     size_t lws_each;
-    size_t o_dA, o_bintra, o_bin, o_ctot;   // offsets inside one layer workspace
+    size_t o_dA, o_bintra, o_bin, o_ctot, o_dblk;   // offsets inside one layer workspace
     const void *dt0, *B0, *C0; // full-sequence dt, B, C
     const float *A0, *D0;      // [n_layers, H]; D0 may be null
     float *states;             // [n_layers, batch, H, P, N]
@@ -69,8 +69,9 @@ struct Problem {
     const float *init;                       // [batch, H, P, N] or null
     float *final_state;                      // [batch, H, P, N] or null
     uint32_t flags;
-    void *dA_cum;      // [batch, H, nc, Q] of CumT<act>
+    void *dA_cum;      // [batch, H, nc, Q] of CumT<act>: log2-domain prefix sums of dt * A
     void *ctot;        // [batch, H, nc] of CumT<act>: each chunk's total (its last dA_cum)
+    float *dblk;       // [batch, H, nc, Q]: decay from each token to the end of its 16-token block
     void *b_intra;     // [batch, nc, H, P*N] act dtype, tile order
     void *b_in;        // [batch, nc, H, P*N] tile order, act dtype
     int heads_per_wg_state;   // head group of chunk_state
@@ -127,6 +128,7 @@ __device__ __forceinline__ Problem step_problem(const Problem &p, int k) {
     unsigned char *w = st.lws + (size_t)slot * st.lws_each;
     q.dA_cum = w + st.o_dA;
     q.ctot = w + st.o_ctot;
+    q.dblk = reinterpret_cast<float *>(w + st.o_dblk);
     q.b_intra = w + st.o_bintra;
     q.b_in = w + st.o_bin;
     return q;
@@ -178,9 +180,17 @@ bool chunk_scan_supported(int dtype, int Q, int P, int N);
 // ---------------------------------------------------------------------------------
 // Type of the log-decay prefix sums: float64 for float32 activations (the differences
 // cum_i - cum_j then keep full fp32 accuracy however large |cum| grows within a chunk),
-// float32 for bfloat16 activations.
+// float32 for bfloat16 activations.  The sums are kept in base 2 (dt * A / ln 2), so every
+// decay exp(sum of dt A) is one hardware 2^x (exp2_fast) with no scaling.
 template <typename T> struct CumT { typedef float type; };
 template <> struct CumT<float> { typedef double type; };
+
+// 1 / ln 2: converts natural-log decay rates dt * A to base 2.
+constexpr double kLog2e = 1.4426950408889634074;
+
+// 2^x with the hardware's transcendental unit (v_exp_f32, ~1 ulp; 0 for x below the
+// smallest representable result).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T> struct TF;
 template <> struct TF<float> { typedef f32x4 type; };

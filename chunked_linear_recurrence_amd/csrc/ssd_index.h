@@ -1,0 +1,145 @@
+// Index arithmetic of the libssdscan kernels that touches memory: which lane copies which
+// 16-byte piece where, and the LDS layouts those copies fill.  The kernels call these
+// functions, and the host program tests/c/index_check.cpp calls the very same ones for
+// every compiled shape, wave, lane and item to check that every global read stays inside
+// its row or tile and every LDS access inside its region (so an index or guard change
+// cannot drift away from what is checked).  Nothing here touches memory.
+#pragma once
+
+#include "ssd_common.h"
+
+namespace ssd {
+
+// ---------------------------------------------------------------------------------
+// chunk_scan: layout constants
+// ---------------------------------------------------------------------------------
+template <typename T, int Q, int P, int N>
+struct ScanCfg {
+    typedef typename CumT<T>::type S;
+    static constexpr int E = (int)sizeof(T);
+    static constexpr int NRB = Q / 16, NW = NRB / 2, THREADS = NW * 64;
+    static constexpr int NSLOT = NRB + 2, NPAIR = NSLOT / 2;
+    static constexpr int NTRI = NRB * (NRB + 1) / 2;            // causal tiles per chunk
+    static constexpr int PT = P / 16, NT = N / 16;
+    // one head's inputs in LDS (HeadBuf): x tile [Q][P], b(c-1) tile [P*N], the prefix
+    // sums cum [Q] and the block decays dblk [Q] (float32)
+    static constexpr int X = Q * P * E, ST = P * N * E, CM = Q * (int)sizeof(S), DL = Q * 4;
+    static constexpr int O_ST = X, O_CM = X + ST, O_DL = O_CM + CM;
+    static constexpr int HEAD_BYTES = O_DL + DL;
+    static constexpr bool DB = 2 * HEAD_BYTES <= kLdsBytes;     // double-buffered head data
+    static constexpr int XPIECES = P * E / 16;                  // 16-byte pieces per x row
+    static constexpr int YPIECES = P * E / 16;                  // 16-byte pieces per output row
+    static constexpr int YW = 32 * P * E;                       // one wave's staged outputs
+    static constexpr bool YS = DB && 2 * HEAD_BYTES + NW * YW <= kLdsBytes;
+    static constexpr int LDS = (DB ? 2 * HEAD_BYTES : HEAD_BYTES) + (YS ? NW * YW : 0);
+    // The chunk's B tile (Q x N) is staged in LDS for the S^T products when it fits beside
+    // the first head's buffer; otherwise the B fragments are loaded from L2.
+    static constexpr int BPIECES = N * E / 16;                  // 16-byte pieces per B row
+    static constexpr bool BL = DB && Q * N * E <= LDS - HEAD_BYTES;
+    // memory work per head and wave, in single-instruction items (64 lanes x 16 bytes)
+    static constexpr int XK = (Q * XPIECES + THREADS - 1) / THREADS;   // x tile
+    static constexpr int SP = ST / 16, SK = (SP + THREADS - 1) / THREADS;  // b(c-1) tile
+    static constexpr int CP = CM / 16, DP = DL / 16;                  // cum, dblk rows
+    static constexpr int NDMA = XK + SK + 2;
+    static constexpr int BK = (Q * BPIECES + THREADS - 1) / THREADS;  // B tile (per workgroup)
+    static constexpr int NSTQ = 32 * YPIECES / 64;                    // staged-output stores
+    static constexpr bool OK = LDS <= kLdsBytes &&
+                               (sizeof(T) == 4 || NT % 2 == 0) && (Q == 32 || Q == 64 || Q == 128 || Q == 256) &&
+                               P * E >= 32 && CP <= THREADS && DP <= THREADS;
+};
+
+// Every (Q, P, N) compiled for chunk_scan, for each activation type T (X(T, Q, P, N)).
+#define SSD_SCAN_SHAPES(X, T)                                                              \
+    X(T, 32, 32, 64) X(T, 32, 64, 64) X(T, 32, 64, 128)                                    \
+    X(T, 64, 16, 16) X(T, 64, 16, 32) X(T, 64, 16, 64) X(T, 64, 16, 128)                   \
+    X(T, 64, 32, 32) X(T, 64, 32, 64) X(T, 64, 32, 128) X(T, 64, 64, 64) X(T, 64, 64, 128) \
+    X(T, 128, 32, 64) X(T, 128, 64, 64) X(T, 128, 64, 128)                                 \
+    X(T, 256, 16, 32) X(T, 256, 32, 64) X(T, 256, 64, 64) X(T, 256, 64, 128)               \
+    X(T, 256, 128, 128) X(T, 256, 64, 256)
+
+// One lane's part of a 64-lane global -> LDS copy of 16-byte pieces: whether it copies,
+// the source row and 16-byte piece within that row (or the piece of a flat tile), and the
+// byte offset it fills in its LDS region (the copy writes lane l at base + 16 l).
+struct DmaPiece {
+    bool on;
+    int row, piece, lds;
+};
+
+// x tile in LDS: row-major [Q][P] in 16-byte pieces; piece q of row r is stored at position
+// q ^ x_swz(r) of that row (bf16), which spreads the 4 rows read by one transpose load over
+// different banks.  pieces = XPIECES is a power of two.
+__host__ __device__ constexpr int x_swz(int r, int pieces) { return (((r >> 1) & 3) << 1) & (pieces - 1); }
+
+// x tile, item k (< XK) of wave w.  The source row may lie past a short chunk; the kernel
+// reads min(row, Qc - 1) instead (those rows only meet zero weights).
+__host__ __device__ constexpr DmaPiece scan_x_piece(int k, int w, int lane, int NW, int Q, int xpieces, bool swz) {
+    const int blk = (k * NW + w) * 64;
+    const int piece = blk + lane;
+    const int r = piece / xpieces;
+    return DmaPiece{blk < Q * xpieces, r, (piece % xpieces) ^ (swz ? x_swz(r, xpieces) : 0), piece * 16};
+}
+
+// A flat tile of `pieces` pieces (b(c-1) in tile order), item kk (< SK) of wave w; the
+// tile is a whole number of waves, so the guard is uniform.
+__host__ __device__ constexpr DmaPiece scan_flat_piece(int kk, int w, int lane, int NW, int pieces) {
+    const int blk = (kk * NW + w) * 64;
+    return DmaPiece{blk < pieces, 0, blk + lane, (blk + lane) * 16};
+}
+
+// A short row of `pieces` pieces (cum or dblk of one (head, chunk)) copied by wave wv.  The
+// row need not fill whole waves (Q < 256), so the guard is per lane then: no lane reads past
+// the row or writes past its LDS region.
+__host__ __device__ constexpr DmaPiece scan_row_piece(int wv, int lane, int pieces) {
+    const int pc = wv * 64 + lane;
+    return DmaPiece{(pieces % 64 == 0) ? (wv * 64 < pieces) : (pc < pieces), 0, pc, pc * 16};
+}
+
+// B tile in LDS: row-major [Q][N], piece q of row j at position q ^ (j & bmask), so the 16
+// rows read by one fragment load hit different banks.
+__host__ __device__ constexpr int b_mask(int bpieces) { return (bpieces < 16 ? bpieces : 16) - 1; }
+
+// B tile, item k (< BK) of wave w (rows past a short chunk: the kernel reads the last row,
+// and the fragments it builds from them are zeroed).
+__host__ __device__ constexpr DmaPiece scan_b_piece(int k, int w, int lane, int NW, int Q, int bpieces) {
+    const int blk = (k * NW + w) * 64;
+    const int slot = blk + lane;
+    const int j = slot / bpieces;
+    return DmaPiece{blk < Q * bpieces, j, (slot % bpieces) ^ (j & b_mask(bpieces)), slot * 16};
+}
+
+// Staged outputs of one wave: 32 rows (its two row blocks) of YPIECES 16-byte pieces; piece
+// q of row r sits at position q ^ ysw(r), so the fragment writes and the row reads both
+// spread over all banks.
+__host__ __device__ constexpr int ysw(int r, int ypieces) { return r & ((ypieces < 8 ? ypieces : 8) - 1); }
+
+// Store item k (< NSTQ) of a wave's staged rows: the staging row (0..31; rows 0..15 are
+// tokens of row block I0, 16..31 of I1), the 16-byte piece of the output row, and the LDS
+// byte offset it is read from.
+__host__ __device__ constexpr DmaPiece scan_y_piece(int k, int lane, int ypieces) {
+    const int pc = k * 64 + lane;
+    const int row = pc / ypieces, q = pc % ypieces;
+    return DmaPiece{true, row, q, (row * ypieces + (q ^ ysw(row, ypieces))) * 16};
+}
+
+// LDS byte offset of the staged output value (row, byte) written by the fragment stores:
+// row = ri * 16 + token within the block, byte = channel * sizeof(T).
+__host__ __device__ constexpr int scan_y_stage(int row, int byte, int ypieces) {
+    return (row * ypieces + ((byte >> 4) ^ ysw(row, ypieces))) * 16 + (byte & 15);
+}
+
+// ---------------------------------------------------------------------------------
+// state_pass: element e (a multiple of 4) of a P x N state in tile order ->
+// (p, first n of the 4 consecutive n held there).  Tile order: 16x16 tiles indexed
+// [n / 16][p / 16], 64 lanes x 4 values each; lane l, value r holds p = 16 pt + l % 16,
+// n = 16 nt + 4 (l / 16) + r.
+// ---------------------------------------------------------------------------------
+struct StateIdx {
+    int p, n0;
+};
+__host__ __device__ constexpr StateIdx tile_elem(int e, int P) {
+    const int tile = e >> 8, l = (e >> 2) & 63;
+    const int PT = P >> 4;
+    return StateIdx{(tile % PT) * 16 + (l & 15), (tile / PT) * 16 + 4 * (l >> 4)};
+}
+
+}  // namespace ssd

@@ -1,7 +1,7 @@
 // state_pass: the sequential pass of global states across chunks, [分块推理 §2.2] of the
 // page "分块推理：解锁循环模型并行计算，实现长序列高效处理":
 //
-//     b(-1) = init_state (or 0),   b(c) = b_intra(c) + exp(total of dA_cum over chunk c) * b(c-1)
+//     b(-1) = init_state (or 0),   b(c) = b_intra(c) + 2^(chunk c's total of dA_cum) * b(c-1)
 //
 // It writes b_in[c] = b(c-1), the state entering chunk c, and final_state = b(nc-1) in
 // float32.  b_intra and b_in are stored in the activation dtype (what chunk_scan's matrix
@@ -20,7 +20,7 @@
 // b_intra and b_in use the tile order of the other kernels (see libssdscan.h); only
 // init_state / final_state use the row-major [P][N] order, so the thread owning tile
 // element (tile, lane l, r = 0..3) maps to p = 16 * pt + l % 16, n = 16 * nt + 4 (l / 16) + r.
-#include "ssd_common.h"
+#include "ssd_index.h"
 
 namespace ssd {
 
@@ -57,11 +57,8 @@ __global__ __launch_bounds__(64) void state_pass_kernel(Problem p0) {
     const int h = blockIdx.y, b = blockIdx.z % p0.batch;
     if (e4 * 4 >= PN) return;
     const int e = e4 * 4;
-    const int tile = e >> 8, l = (e >> 2) & 63;
-    const int PT = p.P >> 4;
-    const int pt = tile % PT, nt = tile / PT;
-    const int pp = pt * 16 + (l & 15), n0 = nt * 16 + 4 * (l >> 4);
-    const int64_t std_off = (((int64_t)b * p.H + h) * p.P + pp) * p.N + n0;
+    const StateIdx pn = tile_elem(e, p.P);                     // (p, n0) of tile-order element e
+    const int64_t std_off = (((int64_t)b * p.H + h) * p.P + pn.p) * p.N + pn.n0;
 
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.init) s = *reinterpret_cast<const float4 *>(p.init + std_off);
@@ -87,7 +84,7 @@ __global__ __launch_bounds__(64) void state_pass_kernel(Problem p0) {
         for (int u = 0; u < K; ++u)
             if (c0 + u < nc) {
                 store_state<T>(bo + (int64_t)(c0 + u) * cstride, s);
-                s = fma4(expf((float)d[u]), s, as_float4(v[u]));
+                s = fma4(exp2_fast((float)d[u]), s, as_float4(v[u]));
             }
     };
     load(0, va, da);

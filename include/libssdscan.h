@@ -123,7 +123,8 @@ typedef struct ssd_dims {
 
 /* Size in bytes of the workspace ssd_chunk_scan_fwd needs for these dims and chunk_Q,
  * or 0 when the arguments are invalid.  The workspace holds the per-chunk log-decay
- * prefix sums (with each chunk's total) and two per-chunk state buffers (nheads * headdim *
+ * prefix sums (with each chunk's total), each token's decay to the end of its 16-token
+ * block (4 bytes per token and head), and two per-chunk state buffers (nheads * headdim *
  * dstate * 2 * act bytes / chunk_Q bytes per token). */
 size_t ssd_chunk_scan_workspace_bytes(const ssd_dims_t *dims, int32_t chunk_Q);
 
@@ -242,9 +243,9 @@ ssd_status_t ssd_chunk_scan_stages(const ssd_dims_t *dims, const void *x, const 
 
 /* Byte offsets of the intermediates inside the workspace:
  *   offsets[0]  dA_cum   [batch, nheads, nchunks, chunk_Q], float64 for SSD_F32 and float32
- *               for SSD_BF16 activations: sum of dt*A from the
- *               chunk start to each token, inclusive (past a short last chunk: the chunk
- *               total);
+ *               for SSD_BF16 activations: sum of dt*A / ln 2 (the base-2 logarithm of the
+ *               decay) from the chunk start to each token, inclusive (past a short last
+ *               chunk: the chunk total);
  *   offsets[1]  b_intra  act dtype, per (batch, chunk, head) a P x N state in tile order;
  *   offsets[2]  b_in     act dtype, the state entering each chunk, same tile order;
  *   offsets[3]  total workspace bytes.

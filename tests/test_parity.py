@@ -63,7 +63,7 @@ def test_stages_match_oracle_intermediates(dtype, b, L, H, P, N, G, Q):
     nc = (L + Q - 1) // Q
     cdt, ce = (torch.float64, 8) if dtype == "f32" else (torch.float32, 4)
     cum = ws[offs[0]:offs[0] + b * H * nc * Q * ce].view(cdt).reshape(b, H, nc, Q)
-    cum = as_np(cum)
+    cum = as_np(cum) * math.log(2.0)        # the library keeps base-2 sums (dt A / ln 2)
     lc = ref["logcum"]
     valid = ~np.isnan(lc)
     ctol = 1e-12 if dtype == "f32" else 1e-5      # fp64 sums for fp32 activations
