@@ -12,14 +12,17 @@
 //   dblk[b, h, c, i]            2^(dA_cum[e(i)] - dA_cum[i]) with e(i) the last token of
 //                               i's 16-token block: the decay from token i to its block's
 //                               end (float32, <= 1).  chunk_scan factors every decay
-//                               between two tokens of different blocks through it.
+//                               between two tokens of different blocks through it;
+//   wend[b, h, c, i]            2^(dA_cum[last] - dA_cum[i]) for tokens of the chunk, the
+//                               decay from token i to the chunk's end (float32, <= 1), and
+//                               0 past a short last chunk: chunk_state's weights.
 // Sums are float64 for float32 activations (dt * A is then exact) and float32 for
 // bfloat16 activations.
 //
 // Work: one workgroup per (batch, chunk, block of kCumHeads heads), one wave per head.  The
 // Q x kCumHeads tile of dt * A is staged in LDS with coalesced loads; each wave then scans
 // its head: every lane sums its Q/64 consecutive values (one vector read), and a 6-step
-// wave shuffle scan combines the lane totals.  HBM-bound (reads dt once, writes 8 or 12
+// wave shuffle scan combines the lane totals.  HBM-bound (reads dt once, writes 12 or 16
 // bytes per token-head).
 #include "ssd_common.h"
 
@@ -156,12 +159,16 @@ __global__ __launch_bounds__(kCumThreads) void chunk_cumsum_kernel(Problem p0) {
         for (int e = 0; e < E; ++e) cv[e] = (lane * E + e <= last) ? excl + v[e] : lastv;
         // the value at the end of this lane's 16-token block (its last lane's last value)
         const S bend = __shfl(cv[E - 1], ((lane * E) | 15) / E, 64);
-        float dl[E];
+        float dl[E], we[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) dl[e] = exp2_fast((float)(bend - cv[e]));
+        for (int e = 0; e < E; ++e) {
+            dl[e] = exp2_fast((float)(bend - cv[e]));
+            we[e] = (lane * E + e <= last) ? exp2_fast((float)(lastv - cv[e])) : 0.f;
+        }
         if (active) {
             store_run<S, E>(out, cv);
             store_run<float, E>(p.dblk + row + lane * E, dl);
+            store_run<float, E>(p.wend + row + lane * E, we);
         }
         if (lane == 0)                               // the chunk's total, for the state pass
             reinterpret_cast<S *>(p.ctot)[((int64_t)b * p.H + hb + hh) * p.nc + c] = lastv;

@@ -40,7 +40,7 @@
 //     y^T += x^T diag(D + residual) on the matrix cores (D split in a high and a low bf16
 //       part so the skip term keeps fp32 accuracy; K = 16 products).
 // Tiles are paired into 16x16x32 bf16 products (16x16x4 f32 for the fp32 dtype).
-#include "ssd_index.h"
+#include "ssd_tile.h"
 
 namespace ssd {
 
@@ -61,76 +61,12 @@ __device__ __forceinline__ Slot slot_of(int s, int w, int NRB) {
 // ---------------------------------------------------------------------------------
 // chunk_scan: one (batch, chunk, group of heads)
 // ---------------------------------------------------------------------------------
-// Raw LDS pointers for the gfx950 LDS-DMA and transpose-read builtins.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
-
-// 16-byte global -> LDS copy: lane l of the wave writes lds_base + 16 * l.  The copies
-// carry the non-temporal cache policy: every stream this kernel reads is used once per
-// step (measured: the whole step is ~4% faster with the streams marked so).
-constexpr int kCachePolicyNT = 2;
-__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, kCachePolicyNT);
-}
-
-// The per-head copies and stores go through buffer descriptors: a uniform base in scalar
-// registers (rebuilt per head with scalar arithmetic) and a 32-bit per-lane offset, so a
-// lane's address costs one vector register instead of two.  Offsets at or past `bytes`
-// read zeros and drop stores (a bound on top of the kernel's own guards).
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRawBufferWord3 = 0x00020000;     // untyped buffer, 32-bit data format (gfx9 family)
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBufferWord3);
-}
-__device__ __forceinline__ void dma16_buf(rsrc_t r, uint32_t voff, void *lds_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, voff, 0, 0, kCachePolicyNT);
-}
-
-
-// A operand fragment of x^T for (16-token block J, 16-channel tile pt): lane (col, g) gets
-// x[16J + 4g + e][16pt + col], e = 0..3.
+// x^T fragment for (16-token block J, 16-channel tile pt): lane (col, g) gets
+// x[16J + 4g + e][16pt + col], e = 0..3 (tile_frag of the row-major x tile).
 template <typename T, int P>
-__device__ __forceinline__ typename TF<T>::type x_frag(const unsigned char *xs, int J, int pt, int lane);
-
-template <>
-__device__ __forceinline__ bf16x4 x_frag<bf16, 16>(const unsigned char *xs, int J, int pt, int lane) {
-    constexpr int P = 16, PIECES = P * 2 / 16;
-    const int s = lane & 15, g = lane >> 4;
-    const int r = J * 16 + 4 * g + (s >> 2);
-    const int c = pt * 16 + 4 * (s & 3);
-    const int q = (c >> 3) ^ x_swz(r, PIECES);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(xs + r * (P * 2) + q * 16 + (c & 7) * 2));
+__device__ __forceinline__ typename TF<T>::type x_frag(const unsigned char *xs, int J, int pt, int lane) {
+    return tile_frag<T, P>(xs, J, pt, lane);
 }
-#define SSD_XFRAG_BF16(PP)                                                                           \
-    template <>                                                                                      \
-    __device__ __forceinline__ bf16x4 x_frag<bf16, PP>(const unsigned char *xs, int J, int pt, int lane) { \
-        constexpr int PIECES = PP * 2 / 16;                                                          \
-        const int s = lane & 15, g = lane >> 4;                                                      \
-        const int r = J * 16 + 4 * g + (s >> 2);                                                     \
-        const int c = pt * 16 + 4 * (s & 3);                                                         \
-        const int q = (c >> 3) ^ x_swz(r, PIECES);                                                   \
-        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(xs + r * (PP * 2) + q * 16 + (c & 7) * 2)); \
-    }
-SSD_XFRAG_BF16(32)
-SSD_XFRAG_BF16(64)
-SSD_XFRAG_BF16(128)
-#undef SSD_XFRAG_BF16
-
-// fp32: no transpose load for 32-bit data; four scalar reads (no swizzle for fp32 tiles).
-#define SSD_XFRAG_F32(PP)                                                                            \
-    template <>                                                                                      \
-    __device__ __forceinline__ f32x4 x_frag<float, PP>(const unsigned char *xs, int J, int pt, int lane) { \
-        const int col = lane & 15, g = lane >> 4;                                                    \
-        const float *base = reinterpret_cast<const float *>(xs) + (J * 16 + 4 * g) * PP + pt * 16 + col; \
-        f32x4 v;                                                                                     \
-        v[0] = base[0]; v[1] = base[PP]; v[2] = base[2 * PP]; v[3] = base[3 * PP];                   \
-        return v;                                                                                    \
-    }
-SSD_XFRAG_F32(16)
-SSD_XFRAG_F32(32)
-SSD_XFRAG_F32(64)
-SSD_XFRAG_F32(128)
-#undef SSD_XFRAG_F32
 
 // Per-head products of wave W (all slot choices and offsets are compile-time):
 // Z^T scaled by G, the decayed S^T tiles times x^T, and (D + res) x.  hook(k, nbuf, ys)

@@ -1,96 +1,51 @@
 // chunk_state: every chunk's local end state from a zero initial state, b_intra(c) of
 // [分块推理 §2.1] (page "分块推理：解锁循环模型并行计算，实现长序列高效处理"):
 //
-//     b_intra(c)[p][n] = sum_j  2^(cum[last] - cum[j]) * x[j][p] * B[j][n]
+//     b_intra(c)[p][n] = sum_j  w_j * x[j][p] * B[j][n],   w_j = 2^(cum[last] - cum[j])
 //
-// over the chunk's tokens j, where cum is the chunk's dA_cum row (base-2 sums of dt A).  Written as a matrix
-// product it is  b_intra^T = B_c^T (N x Q) * (w . x_c) (Q x P)  with w_j the decay from
-// token j to the chunk end, a K = Q contraction on the matrix cores (bf16 in, fp32
-// accumulate; fp32 in for the fp32 dtype).
+// over the chunk's tokens j, where cum is the chunk's dA_cum row (base-2 sums of dt A) and
+// w_j, the decay from token j to the chunk's end, comes precomputed from chunk_cumsum
+// (wend, 0 past a short chunk).  As a matrix product it is
+//     b_intra^T = (B_c . w)^T (N x Q) * x_c (Q x P),
+// a K = Q contraction on the matrix cores (bf16 in, fp32 accumulate; fp32 in for the fp32
+// dtype).
 //
-// Work: one workgroup per (batch, chunk, group of heads that read the same B).  The B
-// chunk is transposed once into LDS (tokens contiguous per state index n) and every wave
-// keeps its A-operand fragments (its share of the n rows, all Q tokens) in registers for
-// all heads of the group.  Per head, x is scaled by w in fp32, rounded to the activation
-// dtype, transposed into LDS (double-buffered), and read as B-operand fragments; the
-// result tiles are rounded once to the activation dtype and stored in tile order, 4
-// values per lane (coalesced 512 B or 1 KiB per wave).
-// The next head's x rows and decays are loaded into registers as soon as the current
-// head's x is in LDS, so their HBM latency overlaps the current head's products.
-#include "ssd_common.h"
+// Work: one workgroup per (batch, chunk, group of heads that read the same B), N/32 waves;
+// wave w owns n tiles [w NTW, (w + 1) NTW) and all P/16 p tiles of the output.
+//   - Once per workgroup the chunk's B tile arrives in LDS by DMA (row-major, swizzled
+//     16-byte pieces), and each wave reads its B^T fragments (k = token) with the gfx950
+//     transpose read and keeps them in registers for every head of the group.
+//   - Per head, the x tile and the wend row arrive in LDS by DMA, double-buffered: the
+//     next head's copies are issued at the start of the current head's products.  x fragments
+//     (k = token) come straight from the transpose read; the weights are applied to the
+//     wave's B^T fragments in fp32 and rounded once to the operand dtype, so no tile is
+//     rewritten in LDS.
+//   - The result tiles are rounded once to the activation dtype and stored in tile order,
+//     4 values per lane (coalesced 512 B or 1 KiB per wave), during the next head.
+#include "ssd_tile.h"
 
 namespace ssd {
 
-template <typename T, int Q, int P, int N>
-struct StateCfg {
-    static constexpr int NT = N / 16, PT = P / 16, KT = Q / 16;
-    static constexpr int NWS = N >= 32 ? N / 32 : 1;          // waves
-    static constexpr int NTW = NT / NWS;                       // n tiles per wave
-    static constexpr int THREADS = NWS * 64;
-    static constexpr int RS = Q + 4;                           // LDS row stride (elements)
-    static constexpr int RJ = 16 / (int)sizeof(T);             // rows per transpose block
-    static constexpr int CW = 16 / (int)sizeof(T);             // columns per block (16-byte rows)
-    static constexpr int XB = (Q / RJ) * (P / CW);             // x transpose blocks
-    static constexpr int XBT = (XB + THREADS - 1) / THREADS;
-    static constexpr int BB = (Q / RJ) * (N / CW);
-    static constexpr int BT_BYTES = N * RS * (int)sizeof(T);
-    static constexpr int XW_BYTES = P * RS * (int)sizeof(T);
-    static constexpr int LDS = BT_BYTES > 2 * XW_BYTES ? BT_BYTES : 2 * XW_BYTES;
-    static constexpr bool OK = (KT % 2 == 0) && LDS <= kLdsBytes && NT % NWS == 0;
-};
-
-// 16 bytes of one row: 8 bf16 or 4 float.
-template <typename T> struct Row16T;
-template <> struct Row16T<bf16> { typedef bf16x8 type; };
-template <> struct Row16T<float> { typedef f32x4 type; };
-
-// Loads rows [j0, j0 + RJ) x cols [c0, c0 + 16 bytes) of a token-major tile (row pitch
-// `pitch` elements), zero past `rows`.  Non-temporal: x and B are streamed once here.
-template <typename T, int RJ>
-__device__ __forceinline__ void load_block(const T *base, int64_t pitch, int j0, int c0, int rows,
-                                           typename Row16T<T>::type (&r)[RJ]) {
-    typedef typename Row16T<T>::type V;
+template <typename T>
+__device__ __forceinline__ typename TF<T>::type scale_frag(const typename TF<T>::type &a, const f32x4 &w) {
+    typename TF<T>::type r;
 #pragma unroll
-    for (int i = 0; i < RJ; ++i) {
-        if (j0 + i < rows) r[i] = __builtin_nontemporal_load(reinterpret_cast<const V *>(base + (int64_t)(j0 + i) * pitch + c0));
-        else r[i] = V{};
-    }
-}
-
-// Writes the transpose of an RJ x CW block into LDS rows c0..c0+CW-1 at column j0,
-// optionally scaling row i by w[i] (in fp32, then rounded to T).
-template <typename T, int RJ, int RS, bool SCALE>
-__device__ __forceinline__ void store_block_t(T *lds, int j0, int c0, const typename Row16T<T>::type (&r)[RJ],
-                                              const float *w) {
-    constexpr int CW = 16 / (int)sizeof(T);
-#pragma unroll
-    for (int cc = 0; cc < CW; ++cc) {
-        typename TF<T>::type col[RJ / 4];
-#pragma unroll
-        for (int i = 0; i < RJ; ++i) {
-            T v = r[i][cc];
-            if (SCALE) v = from_f32<T>(to_f32(v) * w[i]);
-            col[i / 4][i % 4] = v;
-        }
-#pragma unroll
-        for (int q = 0; q < RJ / 4; ++q)
-            *reinterpret_cast<typename TF<T>::type *>(lds + (c0 + cc) * RS + j0 + 4 * q) = col[q];
-    }
+    for (int e = 0; e < 4; ++e) r[e] = from_f32<T>(to_f32(a[e]) * w[e]);
+    return r;
 }
 
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_kernel(Problem p0) {
+__global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS), 2) void chunk_state_kernel(Problem p0) {
     const Problem p = step_problem(p0, blockIdx.y);
     using Cfg = StateCfg<T, Q, P, N>;
     using F = typename TF<T>::type;
-    typedef typename CumT<T>::type S;
-    constexpr int RJ = Cfg::RJ, RS = Cfg::RS, THREADS = Cfg::THREADS;
+    constexpr int NW = Cfg::NWS, NTW = Cfg::NTW, PT = Cfg::PT, KT = Cfg::KT;
+    constexpr int XK = Cfg::XK, NDMA = Cfg::NDMA, XPIECES = Cfg::XPIECES;
     extern __shared__ __align__(16) unsigned char smem[];
-    T *bt = reinterpret_cast<T *>(smem);                    // [N][RS], then reused:
-    T *xw0 = reinterpret_cast<T *>(smem);                   // [P][RS] x 2 buffers
-    T *xw1 = reinterpret_cast<T *>(smem + Cfg::XW_BYTES);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+    const int g4 = 4 * (lane >> 4);
     const int hpg = p.H / p.G;                                // heads per B group
     const int hg_per_group = (hpg + p.heads_per_wg_state - 1) / p.heads_per_wg_state;
     const int nhg = p.G * hg_per_group;
@@ -106,114 +61,123 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS)) void chunk_state_k
     const int Qc = min(Q, p.L - t0);
     const int HP = p.H * P;
 
-    const T *xb = reinterpret_cast<const T *>(p.x) + (int64_t)b * p.x_bs + (int64_t)t0 * HP;
-    const S *cumb = reinterpret_cast<const S *>(p.dA_cum) + ((int64_t)b * p.H) * p.nc * Q + (int64_t)c * Q;
-
-    // x rows and decays of one head, loaded into registers one head ahead of their use
-    typedef typename Row16T<T>::type V;
-    constexpr int CW = Cfg::CW;
-    V xr[Cfg::XBT][RJ];
-    S cw[Cfg::XBT][RJ];
-    S clast = 0;
-    auto prefetch = [&](int h, V (&xv)[Cfg::XBT][RJ], S (&cv)[Cfg::XBT][RJ], S &cl) {
-        const T *xh = xb + h * P;
-        const S *cu = cumb + (int64_t)h * p.nc * Q;
+    // Per-lane byte offsets of this lane's x pieces inside one head's slice of the chunk
+    // (the same for every head), 32 bits (the host bounds a chunk's span of x below 2^31).
+    const unsigned char *xchunk = reinterpret_cast<const unsigned char *>(p.x) +
+                                  ((int64_t)b * p.x_bs + (int64_t)t0 * HP) * (int64_t)sizeof(T);
+    const uint32_t xrow = (uint32_t)(HP * (int)sizeof(T)), xhead = (uint32_t)(P * (int)sizeof(T));
+    uint32_t xoff[XK];
 #pragma unroll
-        for (int k = 0; k < Cfg::XBT; ++k) {
-            const int blk = tid + k * THREADS;
-            if (blk < Cfg::XB) {
-                const int jb = blk / (P / CW), pb = blk % (P / CW);
-                load_block<T, RJ>(xh, HP, jb * RJ, pb * CW, Qc, xv[k]);
-                // the block's RJ consecutive decay sums, as 16-byte loads
-                if constexpr (sizeof(S) == 4) {
-#pragma unroll
-                    for (int q = 0; q < RJ / 4; ++q) {
-                        const float4 u = reinterpret_cast<const float4 *>(cu + jb * RJ)[q];
-                        cv[k][4 * q + 0] = u.x;
-                        cv[k][4 * q + 1] = u.y;
-                        cv[k][4 * q + 2] = u.z;
-                        cv[k][4 * q + 3] = u.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < RJ / 2; ++q) {
-                        const double2 u = reinterpret_cast<const double2 *>(cu + jb * RJ)[q];
-                        cv[k][2 * q + 0] = u.x;
-                        cv[k][2 * q + 1] = u.y;
-                    }
-                }
+    for (int k = 0; k < XK; ++k) {
+        const DmaPiece d = scan_x_piece(k, w, lane, NW, Q, XPIECES, sizeof(T) == 2);
+        const int rr = min(d.row, Qc - 1);                      // rows past a short chunk repeat the last
+        xoff[k] = (uint32_t)rr * xrow + (uint32_t)(d.piece * 16);
+    }
+    // DMA item k of head h into buffer buf: x pieces, then the wend row (waves from NW - 1
+    // down).  Each source is one buffer covering exactly this (head, chunk)'s data.
+    auto dma_item = [&](int k, int h, unsigned char *buf) {
+        if (k < XK) {
+            const DmaPiece d = scan_x_piece(k, w, lane, NW, Q, XPIECES, sizeof(T) == 2);
+            if (d.on)                                           // uniform (whole waves of pieces)
+                dma16_buf(make_rsrc(xchunk + (int64_t)h * xhead, (uint32_t)(Qc - 1) * xrow + xhead), xoff[k],
+                          buf + d.lds - lane * 16);
+        } else {
+            const DmaPiece d = scan_row_piece(NW - 1 - w, lane, Cfg::WP);
+            if (d.on) {
+                const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
+                dma16_buf(make_rsrc(p.wend + tok, Cfg::WB), (uint32_t)(d.piece * 16),
+                          buf + Cfg::O_W + d.lds - lane * 16);
             }
         }
-        cl = cu[Q - 1];
     };
-    prefetch(h0, xr, cw, clast);
 
-    // B chunk -> LDS, transposed: bt[n][j]
+    // ---- per workgroup: the chunk's B tile into LDS, this wave's B^T fragments into
+    // registers.  Rows past a short chunk repeat the last row; their weights are 0.
+    F af[NTW][KT];
     {
-        const T *Bb = reinterpret_cast<const T *>(p.B) + (int64_t)b * p.bc_bs + (int64_t)t0 * p.G * N + grp * N;
-        for (int blk = tid; blk < Cfg::BB; blk += THREADS) {
-            const int jb = blk / (N / CW), nb = blk % (N / CW);
-            V r[RJ];
-            load_block<T, RJ>(Bb, (int64_t)p.G * N, jb * RJ, nb * CW, Qc, r);
-            store_block_t<T, RJ, RS, false>(bt, jb * RJ, nb * CW, r, nullptr);
+        const int64_t bcp = (int64_t)p.G * N;
+        const unsigned char *Bb = reinterpret_cast<const unsigned char *>(p.B) +
+                                  ((int64_t)b * p.bc_bs + (int64_t)t0 * bcp + grp * N) * (int64_t)sizeof(T);
+#pragma unroll
+        for (int k = 0; k < Cfg::BK; ++k) {
+            const DmaPiece d = scan_x_piece(k, w, lane, NW, Q, Cfg::BPIECES, sizeof(T) == 2);
+            if (d.on)                                           // uniform
+                dma16(Bb + (int64_t)min(d.row, Qc - 1) * bcp * (int64_t)sizeof(T) + d.piece * 16,
+                      smem + d.lds - lane * 16);
         }
-    }
-    __syncthreads();
-    F af[Cfg::NTW][Cfg::KT];
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int i = 0; i < Cfg::NTW; ++i) {
-        const int n = (wave * Cfg::NTW + i) * 16 + (lane & 15);
+        for (int i = 0; i < NTW; ++i)
 #pragma unroll
-        for (int kt = 0; kt < Cfg::KT; ++kt)
-            af[i][kt] = *reinterpret_cast<const F *>(bt + n * RS + kt * 16 + 4 * (lane >> 4));
+            for (int kt = 0; kt < KT; ++kt) af[i][kt] = tile_frag<T, N>(smem, kt, w * NTW + i, lane);
+        // every wave's fragment reads have completed before the head buffers are refilled
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
     }
-    __syncthreads();   // bt is overwritten by the x buffers below
+#pragma unroll
+    for (int k = 0; k < NDMA; ++k) dma_item(k, h0, smem);
 
+    // The result tiles of head h are stored in the middle of head h + 1's products, so the
+    // wait at the top of each head (for its copies) never waits on stores just issued.
     const int64_t PN = (int64_t)P * N;
+    F res[NTW][PT];
+    auto store_results = [&](int hs) {
+        T *out = reinterpret_cast<T *>(p.b_intra) + (((int64_t)b * p.nc + c) * p.H + hs) * PN;
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            const int nt = w * NTW + i;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)     // written once, read by state_pass
+                __builtin_nontemporal_store(res[i][pt], reinterpret_cast<F *>(out + ((nt * PT + pt) * 64 + lane) * 4));
+        }
+    };
     for (int h = h0, it = 0; h < h1; ++h, ++it) {
-        T *xw = (it & 1) ? xw1 : xw0;
-        // scale by the decay to the chunk end, transpose into LDS
-#pragma unroll
-        for (int k = 0; k < Cfg::XBT; ++k) {
-            const int blk = tid + k * THREADS;
-            if (blk < Cfg::XB) {
-                const int jb = blk / (P / CW), pb = blk % (P / CW);
-                float w[RJ];
-#pragma unroll
-                for (int i = 0; i < RJ; ++i) w[i] = exp2_fast((float)(clast - cw[k][i]));
-                store_block_t<T, RJ, RS, true>(xw, jb * RJ, pb * CW, xr[k], w);
-            }
-        }
-        if (h + 1 < h1) prefetch(h + 1, xr, cw, clast);   // overlaps this head's products
-        __syncthreads();
+        const unsigned char *buf = smem + (it & 1) * Cfg::HEAD_BYTES;
+        unsigned char *nbuf = smem + ((it + 1) & 1) * Cfg::HEAD_BYTES;
+        __builtin_amdgcn_s_waitcnt(0);        // this head's copies (and older stores) complete
+        __builtin_amdgcn_s_barrier();         // ... for every wave; the other buffer is free
+        const bool more = h + 1 < h1;
+        const float *wl = reinterpret_cast<const float *>(buf + Cfg::O_W);
 
-        f32x4 acc[Cfg::NTW][Cfg::PT];
+        // the next head's copies go out first, so their latency overlaps all of this head's
+        // products (spreading them through the products left the last ones exposed)
+        if (more) {
 #pragma unroll
-        for (int i = 0; i < Cfg::NTW; ++i)
+            for (int k = 0; k < NDMA; ++k) dma_item(k, h + 1, nbuf);
+        }
+        f32x4 acc[NTW][PT];
 #pragma unroll
-            for (int pt = 0; pt < Cfg::PT; ++pt) acc[i][pt] = zero_frag<f32x4>();
+        for (int i = 0; i < NTW; ++i)
 #pragma unroll
-        for (int kt = 0; kt < Cfg::KT; kt += 2) {
+            for (int pt = 0; pt < PT; ++pt) acc[i][pt] = zero_frag<f32x4>();
 #pragma unroll
-            for (int pt = 0; pt < Cfg::PT; ++pt) {
-                const T *row = xw + (pt * 16 + (lane & 15)) * RS + 4 * (lane >> 4);
-                const F x0 = *reinterpret_cast<const F *>(row + kt * 16);
-                const F x1 = *reinterpret_cast<const F *>(row + (kt + 1) * 16);
+        for (int kp = 0; kp < KT / 2; ++kp) {
+            if (kp == KT / 4 && h > h0) store_results(h - 1);   // the previous head's results
+            const int kt0 = 2 * kp, kt1 = 2 * kp + 1;
+            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(wl + 16 * kt0 + g4);
+            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(wl + 16 * kt1 + g4);
+            F a0[NTW], a1[NTW];
 #pragma unroll
-                for (int i = 0; i < Cfg::NTW; ++i)
-                    acc[i][pt] = mma_pair(af[i][kt], x0, af[i][kt + 1], x1, acc[i][pt]);
+            for (int i = 0; i < NTW; ++i) {
+                a0[i] = scale_frag<T>(af[i][kt0], w0);
+                a1[i] = scale_frag<T>(af[i][kt1], w1);
+            }
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const F x0 = tile_frag<T, P>(buf, kt0, pt, lane);
+                const F x1 = tile_frag<T, P>(buf, kt1, pt, lane);
+#pragma unroll
+                for (int i = 0; i < NTW; ++i) acc[i][pt] = mma_pair(a0[i], x0, a1[i], x1, acc[i][pt]);
             }
         }
-        T *out = reinterpret_cast<T *>(p.b_intra) + (((int64_t)b * p.nc + c) * p.H + h) * PN;
+
 #pragma unroll
-        for (int i = 0; i < Cfg::NTW; ++i) {
-            const int nt = wave * Cfg::NTW + i;
+        for (int i = 0; i < NTW; ++i)
 #pragma unroll
-            for (int pt = 0; pt < Cfg::PT; ++pt)
-                __builtin_nontemporal_store(frag_from_f32<T>(acc[i][pt]),   // written once, read by state_pass
-                                            reinterpret_cast<F *>(out + ((nt * Cfg::PT + pt) * 64 + lane) * 4));
-        }
+            for (int pt = 0; pt < PT; ++pt) res[i][pt] = frag_from_f32<T>(acc[i][pt]);
     }
+    store_results(h1 - 1);
 }
 
 template <typename T, int Q, int P, int N>
@@ -232,14 +196,6 @@ static hipError_t launch_state_t(const Problem &p, hipStream_t s) {
         return hipGetLastError();
     }
 }
-
-#define SSD_STATE_SHAPES(X, T)                                                             \
-    X(T, 32, 32, 64) X(T, 32, 64, 64) X(T, 32, 64, 128)                                    \
-    X(T, 64, 16, 16) X(T, 64, 16, 32) X(T, 64, 16, 64) X(T, 64, 16, 128)                   \
-    X(T, 64, 32, 32) X(T, 64, 32, 64) X(T, 64, 32, 128) X(T, 64, 64, 64) X(T, 64, 64, 128) \
-    X(T, 128, 32, 64) X(T, 128, 64, 64) X(T, 128, 64, 128)                                 \
-    X(T, 256, 16, 32) X(T, 256, 32, 64) X(T, 256, 64, 64) X(T, 256, 64, 128)               \
-    X(T, 256, 128, 128) X(T, 256, 64, 256)
 
 #define SSD_STATE_CASE(T, q, pp, nn) \
     if (p.Q == q && p.P == pp && p.N == nn) return launch_state_t<T, q, pp, nn>(p, s);

@@ -42,7 +42,7 @@ constexpr int kStages = 4;   // chunk_cumsum, chunk_state, state_pass, chunk_sca
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t dA, bintra, bin, ctot, dblk, total;
+    size_t dA, bintra, bin, ctot, dblk, wend, total;
 };
 
 int64_t act_bytes(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
@@ -74,6 +74,10 @@ bool layout_for(const ssd_dims_t &d, int64_t L, int32_t Q, Layout *lo) {
     off += align_up((size_t)bhn * (d.dtype == SSD_F32 ? 8 : 4));
     // per token, the decay to the end of its 16-token block (float32), for chunk_scan
     lo->dblk = off;
+    off += align_up((size_t)t * 4);
+    // per token, the decay to the end of its chunk (float32, 0 past a short chunk), for
+    // chunk_state
+    lo->wend = off;
     off += align_up((size_t)t * 4);
     lo->total = off;
     return true;
@@ -231,6 +235,7 @@ ssd_status_t fwd_impl(const ssd_dims_t *dims, const void *x, const void *dt, con
     p.dA_cum = ws + lo.dA;
     p.ctot = ws + lo.ctot;
     p.dblk = reinterpret_cast<float *>(ws + lo.dblk);
+    p.wend = reinterpret_cast<float *>(ws + lo.wend);
     p.b_intra = ws + lo.bintra;
     p.b_in = ws + lo.bin;
     st = run_layer(p, static_cast<hipStream_t>(stream), first_stage, last_stage);
@@ -439,6 +444,7 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
         q.o_dA = sl.lo.dA;
         q.o_ctot = sl.lo.ctot;
         q.o_dblk = sl.lo.dblk;
+        q.o_wend = sl.lo.wend;
         q.o_bintra = sl.lo.bintra;
         q.o_bin = sl.lo.bin;
         q.dt0 = dt;
@@ -488,6 +494,7 @@ ssd_status_t ssd_chunk_scan_segmented(const ssd_dims_t *dims, int32_t n_layers, 
                 p.dA_cum = lws + sl.lo.dA;
                 p.ctot = lws + sl.lo.ctot;
                 p.dblk = reinterpret_cast<float *>(lws + sl.lo.dblk);
+                p.wend = reinterpret_cast<float *>(lws + sl.lo.wend);
                 p.b_intra = lws + sl.lo.bintra;
                 p.b_in = lws + sl.lo.bin;
                 st = run_layer(p, s, 1, kStages);

@@ -47,7 +47,7 @@ struct Steps {
     size_t act_each;
     unsigned char *lws;        // [depth] layer workspaces of lws_each bytes
     size_t lws_each;
-    size_t o_dA, o_bintra, o_bin, o_ctot, o_dblk;   // offsets inside one layer workspace
+    size_t o_dA, o_bintra, o_bin, o_ctot, o_dblk, o_wend;   // offsets inside one layer workspace
     const void *dt0, *B0, *C0; // full-sequence dt, B, C
     const float *A0, *D0;      // [n_layers, H]; D0 may be null
     float *states;             // [n_layers, batch, H, P, N]
@@ -72,6 +72,7 @@ struct Problem {
     void *dA_cum;      // [batch, H, nc, Q] of CumT<act>: log2-domain prefix sums of dt * A
     void *ctot;        // [batch, H, nc] of CumT<act>: each chunk's total (its last dA_cum)
     float *dblk;       // [batch, H, nc, Q]: decay from each token to the end of its 16-token block
+    float *wend;       // [batch, H, nc, Q]: decay from each token to the chunk's end (0 past it)
     void *b_intra;     // [batch, nc, H, P*N] act dtype, tile order
     void *b_in;        // [batch, nc, H, P*N] tile order, act dtype
     int heads_per_wg_state;   // head group of chunk_state
@@ -129,6 +130,7 @@ __device__ __forceinline__ Problem step_problem(const Problem &p, int k) {
     q.dA_cum = w + st.o_dA;
     q.ctot = w + st.o_ctot;
     q.dblk = reinterpret_cast<float *>(w + st.o_dblk);
+    q.wend = reinterpret_cast<float *>(w + st.o_wend);
     q.b_intra = w + st.o_bintra;
     q.b_in = w + st.o_bin;
     return q;

@@ -79,6 +79,21 @@ __host__ __device__ constexpr DmaPiece scan_x_piece(int k, int w, int lane, int 
     return DmaPiece{blk < Q * xpieces, r, (piece % xpieces) ^ (swz ? x_swz(r, xpieces) : 0), piece * 16};
 }
 
+// Byte offset, inside a row-major [rows][W] bf16 tile stored with x_swz, of the 8 bytes lane
+// `lane` reads for the transposed fragment (16-row block J, 16-column tile ct): lane s of a
+// 16-lane group g reads columns c..c+3 of row r, with r = 16J + 4g + s / 4 and
+// c = 16ct + 4 (s % 4); after the transpose, lane (col, g) holds rows 16J + 4g + e of
+// column 16ct + col.
+struct FragRead {
+    int row, col, off;
+};
+__host__ __device__ constexpr FragRead tile_frag_read(int J, int ct, int lane, int W) {
+    const int s = lane & 15, g = lane >> 4;
+    const int r = J * 16 + 4 * g + (s >> 2);
+    const int c = ct * 16 + 4 * (s & 3);
+    return FragRead{r, c, r * (W * 2) + ((c >> 3) ^ x_swz(r, W * 2 / 16)) * 16 + (c & 7) * 2};
+}
+
 // A flat tile of `pieces` pieces (b(c-1) in tile order), item kk (< SK) of wave w; the
 // tile is a whole number of waves, so the guard is uniform.
 __host__ __device__ constexpr DmaPiece scan_flat_piece(int kk, int w, int lane, int NW, int pieces) {
@@ -126,6 +141,43 @@ __host__ __device__ constexpr DmaPiece scan_y_piece(int k, int lane, int ypieces
 __host__ __device__ constexpr int scan_y_stage(int row, int byte, int ypieces) {
     return (row * ypieces + ((byte >> 4) ^ ysw(row, ypieces))) * 16 + (byte & 15);
 }
+
+// ---------------------------------------------------------------------------------
+// chunk_state: layout constants
+// ---------------------------------------------------------------------------------
+template <typename T, int Q, int P, int N>
+struct StateCfg {
+    static constexpr int E = (int)sizeof(T);
+    static constexpr int NT = N / 16, PT = P / 16, KT = Q / 16;
+    static constexpr int NWS = N >= 32 ? N / 32 : 1;           // waves
+    static constexpr int NTW = NT / NWS;                        // n tiles per wave
+    static constexpr int THREADS = NWS * 64;
+    // one head's inputs in LDS: x tile [Q][P] (row-major, x_swz pieces for bf16) and the
+    // chunk-end decays wend [Q] (float32); double-buffered across heads
+    static constexpr int X = Q * P * E, WB = Q * 4;
+    static constexpr int O_W = X, HEAD_BYTES = X + WB;
+    // the chunk's B tile [Q][N] (row-major, x_swz pieces), read once per workgroup into
+    // fragments, occupies the head buffers before the first head's inputs arrive
+    static constexpr int BT = Q * N * E;
+    static constexpr int LDS = 2 * HEAD_BYTES > BT ? 2 * HEAD_BYTES : BT;
+    static constexpr int XPIECES = P * E / 16, BPIECES = N * E / 16;
+    static constexpr int XK = (Q * XPIECES + THREADS - 1) / THREADS;   // x items per head and wave
+    static constexpr int WP = WB / 16;                                 // wend pieces
+    static constexpr int NDMA = XK + 1;
+    static constexpr int BK = (Q * BPIECES + THREADS - 1) / THREADS;   // B items per workgroup and wave
+    static constexpr bool OK = KT % 2 == 0 && NT % NWS == 0 && LDS <= kLdsBytes && P * E >= 32 &&
+                               N * E >= 32 && WP <= THREADS && (Q * XPIECES) % 64 == 0 &&
+                               (Q * BPIECES) % 64 == 0;
+};
+
+// Every (Q, P, N) compiled for chunk_state (X(T, Q, P, N)).
+#define SSD_STATE_SHAPES(X, T)                                                             \
+    X(T, 32, 32, 64) X(T, 32, 64, 64) X(T, 32, 64, 128)                                    \
+    X(T, 64, 16, 16) X(T, 64, 16, 32) X(T, 64, 16, 64) X(T, 64, 16, 128)                   \
+    X(T, 64, 32, 32) X(T, 64, 32, 64) X(T, 64, 32, 128) X(T, 64, 64, 64) X(T, 64, 64, 128) \
+    X(T, 128, 32, 64) X(T, 128, 64, 64) X(T, 128, 64, 128)                                 \
+    X(T, 256, 16, 32) X(T, 256, 32, 64) X(T, 256, 64, 64) X(T, 256, 64, 128)               \
+    X(T, 256, 128, 128) X(T, 256, 64, 256)
 
 // ---------------------------------------------------------------------------------
 // state_pass: element e (a multiple of 4) of a P x N state in tile order ->

@@ -1,7 +1,7 @@
 // Host check of the kernels' memory index arithmetic (no GPU): every function called here
 // is the one the kernels call (chunked_linear_recurrence_amd/csrc/ssd_index.h), evaluated
-// on the CPU for every compiled chunk_scan shape, both activation types, every wave, lane
-// and item, and chunk lengths 1, Q/2 + 3 and Q.  For each copy it checks that the source
+// on the CPU for every compiled chunk_scan and chunk_state shape, both activation types,
+// every wave, lane and item, and chunk lengths 1, Q/2 + 3 and Q.  For each copy it checks that the source
 // lies inside its row or tile, that the LDS destination lies inside its region, and that
 // the pieces cover their tile exactly once; for the staged outputs, that the rows read
 // back are the ones the fragment stores wrote.  It also checks the state tile order used
@@ -55,6 +55,26 @@ static long check_row(const char *what, RowFn fn, int NW, bool down, int pieces,
     return g_fail - before;
 }
 
+// The transposed fragment reads of a row-major [rows][W] bf16 tile that a 64-lane x_swz copy
+// filled (scan_x_piece): every lane's 8 bytes lie in the tile and hold the 4 columns of the
+// row it asks for.  `rows` = Q, `pieces` = W * 2 / 16.
+static void check_frag_reads(const char *what, const char *shape, int rows, int W, int nrowblk, int ncolt,
+                             int region) {
+    const int pieces = W * 2 / 16;
+    for (int J = 0; J < nrowblk; ++J)
+        for (int ct = 0; ct < ncolt; ++ct)
+            for (int lane = 0; lane < 64; ++lane) {
+                const FragRead f = tile_frag_read(J, ct, lane, W);
+                CHECK(f.row < rows && f.col + 4 <= W, "%s %s: fragment row %d col %d", shape, what, f.row, f.col);
+                CHECK(f.off >= 0 && f.off + 8 <= region, "%s %s: fragment byte %d past %d", shape, what, f.off, region);
+                // the copy put source piece (pos ^ x_swz(row)) of row `row` at position pos
+                const int pos = (f.off - f.row * W * 2) / 16;
+                const int src_piece = pos ^ x_swz(f.row, pieces);
+                CHECK(src_piece == f.col / 8 && (f.off & 15) == (f.col % 8) * 2, "%s %s: fragment reads the wrong columns",
+                      shape, what);
+            }
+}
+
 template <typename T, int Q, int P, int N>
 static void check_scan_shape() {
     using Cfg = ScanCfg<T, Q, P, N>;
@@ -89,6 +109,7 @@ static void check_scan_shape() {
             CHECK(xsrc[i] == 1, "%s x: source piece %d copied %d times", shape, i, xsrc[i]);
             CHECK(xdst[i] == 1, "%s x: LDS slot %d written %d times", shape, i, xdst[i]);
         }
+        if (sizeof(T) == 2) check_frag_reads("x", shape, Q, P, Cfg::NRB, Cfg::PT, Cfg::X);
         // within one head's slice of a chunk of Qc rows: the last byte read (row Qc - 1 after
         // the kernel's clamp) is inside the buffer bound the kernel gives that slice,
         // (Qc - 1) * row_pitch + P * E, for the tightest row pitch H * P = P
@@ -165,7 +186,43 @@ static void check_scan_shape() {
     }
 }
 
+template <typename T, int Q, int P, int N>
+static void check_state_shape() {
+    using Cfg = StateCfg<T, Q, P, N>;
+    if constexpr (Cfg::OK) {
+        char shape[64];
+        snprintf(shape, sizeof(shape), "state %s Q=%d P=%d N=%d", sizeof(T) == 2 ? "bf16" : "f32", Q, P, N);
+        const int NW = Cfg::NWS;
+        CHECK(Cfg::LDS <= kLdsBytes && 2 * Cfg::HEAD_BYTES <= Cfg::LDS && Cfg::BT <= Cfg::LDS, "%s: LDS", shape);
+        // x tile of one head and the B tile of the workgroup: the same 64-lane copy
+        for (int which = 0; which < 2; ++which) {
+            const int pieces = which == 0 ? Cfg::XPIECES : Cfg::BPIECES;
+            const int items = which == 0 ? Cfg::XK : Cfg::BK;
+            const int region = which == 0 ? Cfg::X : Cfg::BT;
+            std::vector<int> seen(Q * pieces, 0);
+            for (int w = 0; w < NW; ++w)
+                for (int lane = 0; lane < 64; ++lane)
+                    for (int k = 0; k < items; ++k) {
+                        const DmaPiece d = scan_x_piece(k, w, lane, NW, Q, pieces, sizeof(T) == 2);
+                        if (!d.on) continue;
+                        CHECK(d.row < Q && d.piece < pieces, "%s %s: row %d piece %d", shape, which ? "B" : "x", d.row,
+                              d.piece);
+                        CHECK(d.lds >= 0 && d.lds + 16 <= region, "%s %s: LDS byte %d", shape, which ? "B" : "x", d.lds);
+                        if (d.row < Q && d.piece < pieces) ++seen[d.row * pieces + d.piece];
+                    }
+            for (int i = 0; i < Q * pieces; ++i)
+                CHECK(seen[i] == 1, "%s %s: piece %d copied %d times", shape, which ? "B" : "x", i, seen[i]);
+        }
+        check_row("wend", scan_row_piece, NW, true, Cfg::WP, Cfg::HEAD_BYTES - Cfg::O_W, Cfg::WB, shape);
+        if (sizeof(T) == 2) {
+            check_frag_reads("x", shape, Q, P, Cfg::KT, Cfg::PT, Cfg::X);
+            check_frag_reads("B", shape, Q, N, Cfg::KT, Cfg::NT, Cfg::BT);
+        }
+    }
+}
+
 #define SSD_CHECK_SHAPE(T, q, pp, nn) check_scan_shape<T, q, pp, nn>();
+#define SSD_CHECK_STATE(T, q, pp, nn) check_state_shape<T, q, pp, nn>();
 
 // A per-wave guard on the row copies, the form that once let lanes past a row shorter than
 // a wave: the check above must reject it.
@@ -192,6 +249,8 @@ static void check_tile_order() {
 int main() {
     SSD_SCAN_SHAPES(SSD_CHECK_SHAPE, bf16)
     SSD_SCAN_SHAPES(SSD_CHECK_SHAPE, float)
+    SSD_STATE_SHAPES(SSD_CHECK_STATE, bf16)
+    SSD_STATE_SHAPES(SSD_CHECK_STATE, float)
     check_tile_order();
     const long checks = g_checks, fails = g_fail;
     // sensitivity: the per-wave guard on the 16-piece cum row of Q = 64 (bf16) overruns
