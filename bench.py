@@ -23,9 +23,11 @@ Besides the headline tokens/s the line carries:
                 step at a time, and the horizontal order), a secondary figure;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores on the same inputs.
 
-Algorithmic bytes count every input a kernel needs once and every output it must write
-once, in the dtype the library stores it in (activations and the per-chunk states b_intra
-and b_in in the activation dtype; decay sums, init and final states float32).
+Algorithmic bytes count every input a kernel reads once and every output it writes once,
+in the dtype the library stores it in (activations and the per-chunk states b_intra and
+b_in in the activation dtype; decay sums, the per-token decay arrays, init and final states
+float32).  The end-to-end figure uses the method's own bytes instead (the compulsory I/O
+plus the per-chunk state exchange), which leave out the library's decay intermediates.
 """
 import argparse
 import json
@@ -81,13 +83,15 @@ def alg_bytes(w):
     dt = b * L * H * e
     bc = b * L * G * N * e                      # one of B or C
     cum = b * H * nc * Q * cum_e                # dA_cum
+    dec = b * H * nc * Q * 4                    # one per-token decay array (block end or chunk end)
+    ctot = b * H * nc * cum_e                   # chunk totals
     states = b * nc * H * P * N
     init = final = b * H * P * N * 4
     k = {
-        "chunk_cumsum": dt + cum,
-        "chunk_state": x + bc + cum + states * e,
-        "state_pass": 2 * states * e + b * H * nc * cum_e + final + (init if w.init != "zero" else 0),
-        "chunk_scan": x + 2 * bc + cum + states * e + y,
+        "chunk_cumsum": dt + cum + 2 * dec + ctot,
+        "chunk_state": x + bc + dec + states * e,
+        "state_pass": 2 * states * e + ctot + final + (init if w.init != "zero" else 0),
+        "chunk_scan": x + 2 * bc + cum + dec + states * e + y,
     }
     compulsory = x + y + dt + 2 * bc + (init if w.init != "zero" else 0) + final
     method = compulsory + 4 * states * e

@@ -5,7 +5,8 @@ rerun on this hardware with synthetic layers.
     python -m chunked_linear_recurrence_amd.sweep [--quick]
 
 prints markdown tables:
-  Q   tokens/s of one layer at the 128K-token shape for chunk_Q in {64, 128, 256};
+  Q   tokens/s of one layer at the 128K-token shape for chunk_Q in {32, 64, 128, 256},
+      with each kernel's time (its stage run on its own) and the launches per step;
   V   layer-tokens/s and memory of a 24-layer stack (batch 1, 32768 tokens; and batch 4,
       8192 tokens) for V from Q up to 8192, in both schedules of ssd_chunk_scan_segmented,
       next to the horizontal order; with the page's rule of thumb (stop doubling V once
@@ -41,19 +42,21 @@ def q_sweep(dev, reps):
     d = inputs.make(w)
     g = {k: (v.to(dev) if v is not None else None) for k, v in d.items()}
     rows = []
-    for Q in (64, 128, 256):
+    for Q in (32, 64, 128, 256):
         dims = ssd.dims_of(g["x"], g["B"])
         if not ssd.shape_supported(dims.dtype, Q, w.headdim, w.dstate):
-            rows.append((Q, None, None))
+            rows.append((Q, None, None, None))
             continue
         ws = ssd.alloc_workspace(ssd.workspace_bytes(dims, Q), dev)
         y = torch.empty_like(g["x"])
         fin = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, device=dev)
 
-        def f():
-            ssd.fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], None, Q, y=y, final_state=fin, workspace=ws)
+        def f(first=1, last=ssd.NSTAGES):
+            ssd.fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], None, Q, y=y, final_state=fin, workspace=ws,
+                    first_stage=first, last_stage=last)
         ms = _time(f, reps, settle=30)
-        rows.append((Q, ms, ws.numel()))
+        stages = [_time(lambda k=k: f(k, k), reps, settle=3) for k in range(1, ssd.NSTAGES + 1)]
+        rows.append((Q, ms, ws.numel(), stages))
         del ws
     return w, rows
 
@@ -113,14 +116,18 @@ def main():
     w, rows = q_sweep(dev, reps)
     print("## Chunk length Q: one layer, %s (batch %d, L %d, H %d, P %d, N %d, %s)\n"
           % (w.name, w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.dtype))
-    print("| Q | ms per layer | M tokens/s | workspace MB |")
-    print("|---|---|---|---|")
-    for Q, ms, wsb in rows:
+    print("| Q | chunks | ms per layer | M tokens/s | workspace MB | chunk_cumsum us | chunk_state us | "
+          "state_pass us | chunk_scan us |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for Q, ms, wsb, stages in rows:
         if ms is None:
-            print("| %d | not compiled | | |" % Q)
+            print("| %d | | not compiled | | | | | | |" % Q)
         else:
-            print("| %d | %.3f | %.1f | %.0f |" % (Q, ms, w.tokens / ms / 1e3, wsb / 1e6))
-    print(flush=True)
+            print("| %d | %d | %.3f | %.1f | %.0f | %s |" % (
+                Q, -(-w.seqlen // Q), ms, w.tokens / ms / 1e3, wsb / 1e6,
+                " | ".join("%.1f" % (t * 1e3) for t in stages)))
+    print("\nEvery Q runs the same 4 launches per layer; smaller Q means more chunks, so more "
+          "per-chunk state traffic (it scales with 1/Q) and a longer serial state pass.", flush=True)
 
     for batch, seqlen in ((1, 32768), (4, 8192)):
         Vs = [256 * 2 ** k for k in range(6)]              # Q .. 8192
