@@ -138,15 +138,32 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 // Work partition: heads per workgroup so that there are at least `target` workgroups
 // (when the problem has that many heads to spread).  Only the split changes, never the
 // arithmetic of any output element.
-int heads_per_wg(int64_t units, int64_t hpg, int64_t target, const char *env) {
+int env_heads(const char *env, int64_t hpg) {
     if (const char *s = getenv(env)) {
         const int v = atoi(s);
         if (v >= 1) return (int)(v < hpg ? v : hpg);
     }
+    return 0;
+}
+
+int heads_per_wg(int64_t units, int64_t hpg, int64_t target, const char *env) {
+    if (const int v = env_heads(env, hpg)) return v;
     int64_t hg = hpg * units / target;
     if (hg < 1) hg = 1;
     if (hg > hpg) hg = hpg;
     return (int)hg;
+}
+
+// chunk_state: the largest divisor of the group's heads, at most 16, that still leaves a
+// full round of resident workgroups (two per CU on 256 CUs).  Equal groups: a ragged last
+// group measured 5-10% slower; 16 heads measured best at the 128K-token layer (238 us
+// against 252 with 24 or 12) and 8 at batch 8 x 4K tokens (50 us against 51.5 with 4).
+int heads_per_wg_state(int64_t units, int64_t hpg) {
+    if (const int v = env_heads("SSD_HEADS_PER_WG_STATE", hpg)) return v;
+    int best = 1;
+    for (int d = 1; d <= 16 && d <= hpg; ++d)
+        if (hpg % d == 0 && units * (hpg / d) >= 512) best = d;
+    return best;
 }
 
 ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q, int steps = 1) {
@@ -165,8 +182,9 @@ ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q, int steps =
     const int64_t hpg = d.nheads / d.ngroups;
     // chunk_scan takes most of a CU's LDS (one workgroup per CU): aim for about one
     // workgroup per CU, which amortises each workgroup's C.B^T tiles over as many heads as
-    // that allows.  chunk_state (two workgroups per CU) measured best with about four per CU.
-    p.heads_per_wg_state = heads_per_wg(units, hpg, 1024, "SSD_HEADS_PER_WG_STATE");
+    // that allows (measured: 48 heads per workgroup at the 128K-token layer, 443 us, against
+    // 460-496 us with 24, 16 or 12; 16 at batch 8 x 4K tokens, 80 us against 93 with 8).
+    p.heads_per_wg_state = heads_per_wg_state(units, hpg);
     p.heads_per_wg_scan = heads_per_wg(units, hpg, 256, "SSD_HEADS_PER_WG_SCAN");
     return p;
 }
