@@ -146,12 +146,20 @@ int env_heads(const char *env, int64_t hpg) {
     return 0;
 }
 
-int heads_per_wg(int64_t units, int64_t hpg, int64_t target, const char *env) {
-    if (const int v = env_heads(env, hpg)) return v;
-    int64_t hg = hpg * units / target;
-    if (hg < 1) hg = 1;
-    if (hg > hpg) hg = hpg;
-    return (int)hg;
+constexpr int64_t kCUs = 256;     // compute units of one MI355X
+
+// chunk_scan takes most of a CU's LDS, so one workgroup runs per CU: the smallest equal
+// split of the group's heads that fits the grid in one round of workgroups (all heads of
+// the group when even that is more than one round).  Fewer heads per workgroup leave the
+// C.B^T tiles amortised over fewer heads; a second round leaves a tail.  Measured: 48 heads
+// per workgroup at the 128K-token layer (443 us, against 460-496 with 24, 16 or 12), 16 at
+// batch 8 x 4K tokens (80 us, against 93 with 8 and 126 with 32), 2 at the Mamba-2-130M
+// layer (batch 2 x 2K tokens: 25 us, against 38 with 1 and 31 with 4).
+int heads_per_wg_scan(int64_t units, int64_t hpg) {
+    if (const int v = env_heads("SSD_HEADS_PER_WG_SCAN", hpg)) return v;
+    for (int d = 1; d < hpg; ++d)
+        if (hpg % d == 0 && units * (hpg / d) <= kCUs) return d;
+    return (int)hpg;
 }
 
 // chunk_state: the largest divisor of the group's heads, at most 16, that still leaves a
@@ -162,7 +170,7 @@ int heads_per_wg_state(int64_t units, int64_t hpg) {
     if (const int v = env_heads("SSD_HEADS_PER_WG_STATE", hpg)) return v;
     int best = 1;
     for (int d = 1; d <= 16 && d <= hpg; ++d)
-        if (hpg % d == 0 && units * (hpg / d) >= 512) best = d;
+        if (hpg % d == 0 && units * (hpg / d) >= 2 * kCUs) best = d;
     return best;
 }
 
@@ -180,12 +188,8 @@ ssd::Problem make_problem(const ssd_dims_t &d, int64_t L, int32_t Q, int steps =
     p.dtype = d.dtype;
     const int64_t units = d.batch * p.nc * d.ngroups * steps;
     const int64_t hpg = d.nheads / d.ngroups;
-    // chunk_scan takes most of a CU's LDS (one workgroup per CU): aim for about one
-    // workgroup per CU, which amortises each workgroup's C.B^T tiles over as many heads as
-    // that allows (measured: 48 heads per workgroup at the 128K-token layer, 443 us, against
-    // 460-496 us with 24, 16 or 12; 16 at batch 8 x 4K tokens, 80 us against 93 with 8).
     p.heads_per_wg_state = heads_per_wg_state(units, hpg);
-    p.heads_per_wg_scan = heads_per_wg(units, hpg, 256, "SSD_HEADS_PER_WG_SCAN");
+    p.heads_per_wg_scan = heads_per_wg_scan(units, hpg);
     return p;
 }
 
