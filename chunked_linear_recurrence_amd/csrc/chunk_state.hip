@@ -10,8 +10,9 @@
 // a K = Q contraction on the matrix cores (bf16 in, fp32 accumulate; fp32 in for the fp32
 // dtype).
 //
-// Work: one workgroup per (batch, chunk, group of heads that read the same B), N/32 waves;
-// wave w owns n tiles [w NTW, (w + 1) NTW) and all P/16 p tiles of the output.
+// Work: one workgroup per (batch, chunk, group of heads that read the same B), N/32 waves,
+// each owning NTW n tiles and all P/16 p tiles of the output; shapes whose LDS allows only
+// one workgroup per CU take twice the waves, each with half of the p tiles (StateCfg).
 //   - Once per workgroup the chunk's B tile arrives in LDS by DMA (row-major, swizzled
 //     16-byte pieces), and each wave reads its B^T fragments (k = token) with the gfx950
 //     transpose read and keeps them in registers for every head of the group.
@@ -35,16 +36,17 @@ __device__ __forceinline__ typename TF<T>::type scale_frag(const typename TF<T>:
 }
 
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS), 2) void chunk_state_kernel(Problem p0) {
+__global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS), (StateCfg<T, Q, P, N>::MINB)) void chunk_state_kernel(Problem p0) {
     const Problem p = step_problem(p0, blockIdx.y);
     using Cfg = StateCfg<T, Q, P, N>;
     using F = typename TF<T>::type;
-    constexpr int NW = Cfg::NWS, NTW = Cfg::NTW, PT = Cfg::PT, KT = Cfg::KT;
+    constexpr int NW = Cfg::NWS, NTW = Cfg::NTW, PT = Cfg::PT, PTW = Cfg::PTW, KT = Cfg::KT;
     constexpr int XK = Cfg::XK, NDMA = Cfg::NDMA, XPIECES = Cfg::XPIECES;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+    const StateTiles tiles = state_wave_tiles(w, Cfg::NWN, NTW, PTW, Cfg::PS);
     const int g4 = 4 * (lane >> 4);
     const int hpg = p.H / p.G;                                // heads per B group
     const int hg_per_group = (hpg + p.heads_per_wg_state - 1) / p.heads_per_wg_state;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS), 2) void chunk_stat
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) af[i][kt] = tile_frag<T, N>(smem, kt, w * NTW + i, lane);
+            for (int kt = 0; kt < KT; ++kt) af[i][kt] = tile_frag<T, N>(smem, kt, tiles.nt0 + i, lane);
         // every wave's fragment reads have completed before the head buffers are refilled
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
@@ -121,15 +123,16 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS), 2) void chunk_stat
     // The result tiles of head h are stored in the middle of head h + 1's products, so the
     // wait at the top of each head (for its copies) never waits on stores just issued.
     const int64_t PN = (int64_t)P * N;
-    F res[NTW][PT];
+    F res[NTW][PTW];
     auto store_results = [&](int hs) {
         T *out = reinterpret_cast<T *>(p.b_intra) + (((int64_t)b * p.nc + c) * p.H + hs) * PN;
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-            const int nt = w * NTW + i;
+            const int nt = tiles.nt0 + i;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt)     // written once, read by state_pass
-                __builtin_nontemporal_store(res[i][pt], reinterpret_cast<F *>(out + ((nt * PT + pt) * 64 + lane) * 4));
+            for (int pt = 0; pt < PTW; ++pt)    // written once, read by state_pass
+                __builtin_nontemporal_store(res[i][pt],
+                                            reinterpret_cast<F *>(out + ((nt * PT + tiles.pt0 + pt) * 64 + lane) * 4));
         }
     };
     for (int h = h0, it = 0; h < h1; ++h, ++it) {
@@ -146,11 +149,11 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS), 2) void chunk_stat
 #pragma unroll
             for (int k = 0; k < NDMA; ++k) dma_item(k, h + 1, nbuf);
         }
-        f32x4 acc[NTW][PT];
+        f32x4 acc[NTW][PTW];
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[i][pt] = zero_frag<f32x4>();
+            for (int pt = 0; pt < PTW; ++pt) acc[i][pt] = zero_frag<f32x4>();
 #pragma unroll
         for (int kp = 0; kp < KT / 2; ++kp) {
             if (kp == KT / 4 && h > h0) store_results(h - 1);   // the previous head's results
@@ -164,9 +167,9 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS), 2) void chunk_stat
                 a1[i] = scale_frag<T>(af[i][kt1], w1);
             }
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const F x0 = tile_frag<T, P>(buf, kt0, pt, lane);
-                const F x1 = tile_frag<T, P>(buf, kt1, pt, lane);
+            for (int pt = 0; pt < PTW; ++pt) {
+                const F x0 = tile_frag<T, P>(buf, kt0, tiles.pt0 + pt, lane);
+                const F x1 = tile_frag<T, P>(buf, kt1, tiles.pt0 + pt, lane);
 #pragma unroll
                 for (int i = 0; i < NTW; ++i) acc[i][pt] = mma_pair(a0[i], x0, a1[i], x1, acc[i][pt]);
             }
@@ -175,7 +178,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, N>::THREADS), 2) void chunk_stat
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) res[i][pt] = frag_from_f32<T>(acc[i][pt]);
+            for (int pt = 0; pt < PTW; ++pt) res[i][pt] = frag_from_f32<T>(acc[i][pt]);
     }
     store_results(h1 - 1);
 }

@@ -149,9 +149,6 @@ template <typename T, int Q, int P, int N>
 struct StateCfg {
     static constexpr int E = (int)sizeof(T);
     static constexpr int NT = N / 16, PT = P / 16, KT = Q / 16;
-    static constexpr int NWS = N >= 32 ? N / 32 : 1;           // waves
-    static constexpr int NTW = NT / NWS;                        // n tiles per wave
-    static constexpr int THREADS = NWS * 64;
     // one head's inputs in LDS: x tile [Q][P] (row-major, x_swz pieces for bf16) and the
     // chunk-end decays wend [Q] (float32); double-buffered across heads
     static constexpr int X = Q * P * E, WB = Q * 4;
@@ -160,15 +157,35 @@ struct StateCfg {
     // fragments, occupies the head buffers before the first head's inputs arrive
     static constexpr int BT = Q * N * E;
     static constexpr int LDS = 2 * HEAD_BYTES > BT ? 2 * HEAD_BYTES : BT;
+    // Waves: N/32 along n, each owning NTW n tiles.  When the LDS leaves room for only one
+    // workgroup per CU (so each SIMD has the registers of two waves) and that makes at most
+    // 8 waves, a second wave per n range takes half of the p tiles: each wave then holds
+    // half the accumulators, which keeps the large tiles (P = 128, fp32 at Q = 256) in
+    // registers.
+    static constexpr int NWN = N >= 32 ? N / 32 : 1;           // waves along n
+    static constexpr int NTW = NT / NWN;                        // n tiles per wave
+    static constexpr int PS = (LDS > kLdsBytes / 2 && NWN <= 4 && PT % 2 == 0) ? 2 : 1;
+    static constexpr int PTW = PT / PS;                         // p tiles per wave
+    static constexpr int NWS = NWN * PS;                        // waves
+    static constexpr int THREADS = NWS * 64;
+    static constexpr int MINB = PS == 2 ? 1 : 2;                // workgroups per CU (launch bound)
     static constexpr int XPIECES = P * E / 16, BPIECES = N * E / 16;
     static constexpr int XK = (Q * XPIECES + THREADS - 1) / THREADS;   // x items per head and wave
     static constexpr int WP = WB / 16;                                 // wend pieces
     static constexpr int NDMA = XK + 1;
     static constexpr int BK = (Q * BPIECES + THREADS - 1) / THREADS;   // B items per workgroup and wave
-    static constexpr bool OK = KT % 2 == 0 && NT % NWS == 0 && LDS <= kLdsBytes && P * E >= 32 &&
+    static constexpr bool OK = KT % 2 == 0 && NT % NWN == 0 && LDS <= kLdsBytes && P * E >= 32 &&
                                N * E >= 32 && WP <= THREADS && (Q * XPIECES) % 64 == 0 &&
                                (Q * BPIECES) % 64 == 0;
 };
+
+// The output tiles of chunk_state's wave w: n tiles [nt0, nt0 + NTW), p tiles [pt0, pt0 + PTW).
+struct StateTiles {
+    int nt0, pt0;
+};
+__host__ __device__ constexpr StateTiles state_wave_tiles(int w, int NWN, int NTW, int PTW, int PS) {
+    return PS == 1 ? StateTiles{w * NTW, 0} : StateTiles{(w % NWN) * NTW, (w / NWN) * PTW};
+}
 
 // Every (Q, P, N) compiled for chunk_state (X(T, Q, P, N)).
 #define SSD_STATE_SHAPES(X, T)                                                             \

@@ -214,6 +214,22 @@ static void check_state_shape() {
                 CHECK(seen[i] == 1, "%s %s: piece %d copied %d times", shape, which ? "B" : "x", i, seen[i]);
         }
         check_row("wend", scan_row_piece, NW, true, Cfg::WP, Cfg::HEAD_BYTES - Cfg::O_W, Cfg::WB, shape);
+        // every output tile (n tile, p tile) owned by exactly one wave
+        CHECK(Cfg::THREADS <= 1024 && Cfg::NWN * Cfg::NTW == Cfg::NT && Cfg::PS * Cfg::PTW == Cfg::PT,
+              "%s: wave split", shape);
+        std::vector<int> tseen(Cfg::NT * Cfg::PT, 0);
+        for (int w = 0; w < NW; ++w) {
+            const StateTiles t = state_wave_tiles(w, Cfg::NWN, Cfg::NTW, Cfg::PTW, Cfg::PS);
+            for (int i = 0; i < Cfg::NTW; ++i)
+                for (int pt = 0; pt < Cfg::PTW; ++pt) {
+                    const int nt = t.nt0 + i, pp = t.pt0 + pt;
+                    CHECK(nt >= 0 && nt < Cfg::NT && pp >= 0 && pp < Cfg::PT, "%s: wave %d tile (%d, %d)", shape, w,
+                          nt, pp);
+                    if (nt >= 0 && nt < Cfg::NT && pp >= 0 && pp < Cfg::PT) ++tseen[nt * Cfg::PT + pp];
+                }
+        }
+        for (int i = 0; i < Cfg::NT * Cfg::PT; ++i)
+            CHECK(tseen[i] == 1, "%s: output tile %d owned by %d waves", shape, i, tseen[i]);
         if (sizeof(T) == 2) {
             check_frag_reads("x", shape, Q, P, Cfg::KT, Cfg::PT, Cfg::X);
             check_frag_reads("B", shape, Q, N, Cfg::KT, Cfg::NT, Cfg::BT);
