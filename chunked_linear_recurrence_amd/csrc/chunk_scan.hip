@@ -1,11 +1,12 @@
 // chunk_scan: every chunk's output, [分块推理 §2.1-§2.2] of the page
 // "分块推理：解锁循环模型并行计算，实现长序列高效处理":
 //
-//   by_intra_i = sum_{j <= i} (C_i . B_j) exp(cum_i - cum_j) x_j      (zero-state intra part)
-//   by_inter_i = exp(cum_i) (b(c-1) C_i)                               (diag(L) C(c) b(c-1))
+//   by_intra_i = sum_{j <= i} (C_i . B_j) 2^(cum_i - cum_j) x_j      (zero-state intra part)
+//   by_inter_i = 2^(cum_i) (b(c-1) C_i)                                (diag(L) C(c) b(c-1))
 //   y_i        = by_intra_i + by_inter_i + D x_i  (+ x_i with SSD_FLAG_RESIDUAL)
 //
-// rounded once to the activation dtype.  cum is the chunk's dA_cum row and b(c-1) is
+// rounded once to the activation dtype.  cum is the chunk's dA_cum row, the base-2 prefix
+// sums of dt A (so 2^(cum_i - cum_j) is the decay from token j to token i), and b(c-1) is
 // b_in[c] from state_pass.
 //
 // One workgroup per (batch, chunk, group of heads that read the same B and C).  A chunk
@@ -22,11 +23,10 @@
 // fp32 registers for every head of the group: C.B^T is formed once per chunk and group,
 // never per head.
 //
-// Per head, x is brought into LDS by DMA (tokens x channels, read back as transposed
-// fragments), b_in likewise, and the chunk's log-decay prefix sums cum and block decays
-// dblk.  The products are
-// computed transposed (y^T[p][i]) so that a lane's 4 accumulator values are 4 consecutive
-// channels of one token:
+// Per head, x is brought into LDS by buffer DMA (tokens x channels, read back as
+// transposed fragments), b_in likewise, and the chunk's prefix sums cum and block decays
+// dblk.  The products are computed transposed (y^T[p][i]) so that a lane's 4 accumulator
+// values are 4 consecutive channels of one token:
 //     Z^T = b(c-1) C^T, column i scaled by G_i = 2^(cum_i);
 //     y^T += x^T (S^T . decay), the decay of tile entry (j, i) being 2^(cum_i - cum_j)
 //       (cum holds base-2 sums of dt A).  Below the diagonal (token j in an earlier 16-token
@@ -96,7 +96,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
 
     // Output tiles are transposed: acc[ri][pt] lane (col, g), value r holds
     // y^T[p = pt*16 + 4g + r][i = I*16 + col].
-    // Z^T = b(c-1) C^T, then column i scaled by G_i = exp(cum_i)
+    // Z^T = b(c-1) C^T, then column i scaled by G_i = 2^(cum_i)
 #pragma unroll
     for (int ri = 0; ri < 2; ++ri)
 #pragma unroll
