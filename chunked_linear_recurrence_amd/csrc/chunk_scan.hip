@@ -25,7 +25,9 @@
 //
 // Per head, x is brought into LDS by buffer DMA (tokens x channels, read back as
 // transposed fragments), b_in likewise, and the chunk's prefix sums cum and block decays
-// dblk.  The products are computed transposed (y^T[p][i]) so that a lane's 4 accumulator
+// dblk.  A head whose inputs do not fit in LDS twice (P = 128; fp32 at Q = 256) is taken as
+// two units of P/2 channels, each a head of its own for the copies, products and stores
+// (ScanCfg::PS), so those shapes are double-buffered too.  The products are computed transposed (y^T[p][i]) so that a lane's 4 accumulator
 // values are 4 consecutive channels of one token:
 //     Z^T = b(c-1) C^T, column i scaled by G_i = 2^(cum_i);
 //     y^T += x^T (S^T . decay), the decay of tile entry (j, i) being 2^(cum_i - cum_j)
@@ -162,8 +164,8 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
         const bool owner1 = (2 * q) >= (w + 1);             // uniform
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const F x0 = x_frag<T, P>(xs, Jx[0], pt, lane);
-            const F x1 = x_frag<T, P>(xs, Jx[1], pt, lane);
+            const F x0 = x_frag<T, Cfg::PV>(xs, Jx[0], pt, lane);
+            const F x1 = x_frag<T, Cfg::PV>(xs, Jx[1], pt, lane);
             if (owner1) acc[1][pt] = mma_pair(x0, a[0], x1, a[1], acc[1][pt]);
             else acc[0][pt] = mma_pair(x0, a[0], x1, a[1], acc[0][pt]);
         }
@@ -187,7 +189,7 @@ __device__ __forceinline__ void scan_head(const unsigned char *__restrict__ buf,
             for (int pt = 0; pt < PT; ++pt) {
                 // K = 16 products: x's fragment is the A operand as it is (a K = 32 product
                 // would need it twice in consecutive registers)
-                const F xv = x_frag<T, P>(xs, I, pt, lane);
+                const F xv = x_frag<T, Cfg::PV>(xs, I, pt, lane);
                 acc[ri][pt] = mma_one(xv, dhi, acc[ri][pt]);
                 if constexpr (sizeof(T) == 2) acc[ri][pt] = mma_one(xv, dlo, acc[ri][pt]);
             }
@@ -204,6 +206,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     constexpr int NW = Cfg::NW;
     constexpr int NRB = Cfg::NRB, NSLOT = Cfg::NSLOT, PT = Cfg::PT, NT = Cfg::NT;
     constexpr int XPIECES = Cfg::XPIECES, YPIECES = Cfg::YPIECES;
+    constexpr int PS = Cfg::PS, PV = Cfg::PV;    // units per head, channels per unit
     // memory work per head and wave, in single-instruction items (Cfg): XK x pieces, SK
     // b_in pieces, one cum row, one dblk row, then NSTQ staged-output stores
     constexpr int XK = Cfg::XK, SK = Cfg::SK, NDMA = Cfg::NDMA, NSTQ = Cfg::NSTQ;
@@ -235,10 +238,11 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
 
     const unsigned char *xchunk = reinterpret_cast<const unsigned char *>(p.x) +
                                   ((int64_t)b * p.x_bs + (int64_t)t0 * HP) * (int64_t)sizeof(T);
-    // Per-lane byte offsets of this lane's x pieces inside one head's slice of the chunk
-    // (the same for every head: the head only moves the uniform base), kept in 32 bits
+    // Per-lane byte offsets of this lane's x pieces inside one unit's slice of the chunk
+    // (the same for every unit: the unit only moves the uniform base), kept in 32 bits
     // (the host bounds a chunk's span of x, Q * H * P * sizeof(T), below 2^31).
-    const uint32_t xrow = (uint32_t)(HP * (int)sizeof(T)), xhead = (uint32_t)(P * (int)sizeof(T));
+    const uint32_t xrow = (uint32_t)(HP * (int)sizeof(T)), xunit = (uint32_t)(PV * (int)sizeof(T));
+    const uint32_t xhead = (uint32_t)(P * (int)sizeof(T));
     uint32_t xoff[XK];
 #pragma unroll
     for (int k = 0; k < XK; ++k) {
@@ -246,21 +250,23 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         const int rr = min(d.row, Qc - 1);                      // rows past a short chunk repeat the last
         xoff[k] = (uint32_t)rr * xrow + (uint32_t)(d.piece * 16);
     }
-    // DMA item k of head h into buffer buf (indices from ssd_index.h): x pieces, then b_in
-    // pieces, then the cum row (waves from 0 up) and the dblk row (waves from NW - 1 down).
-    // Each source is one buffer covering exactly this (head, chunk)'s data.
-    auto dma_item = [&](int k, int h, unsigned char *buf) {
+    // DMA item k of unit (h, half) into buffer buf (indices from ssd_index.h): x pieces,
+    // then b_in pieces, then the cum row (waves from 0 up) and the dblk row (waves from
+    // NW - 1 down).  Each source is one buffer covering exactly this (head, chunk)'s data
+    // (x: the unit's channels).
+    auto dma_item = [&](int k, int h, int half, unsigned char *buf) {
         if (k < XK) {
             const DmaPiece d = scan_x_piece(k, w, lane, NW, Q, XPIECES, sizeof(T) == 2);
             if (d.on)                                           // uniform (whole waves of pieces)
-                dma16_buf(make_rsrc(xchunk + (int64_t)h * xhead, (uint32_t)(Qc - 1) * xrow + xhead), xoff[k],
-                          buf + d.lds - lane * 16);
+                dma16_buf(make_rsrc(xchunk + (int64_t)h * xhead + half * xunit, (uint32_t)(Qc - 1) * xrow + xunit),
+                          xoff[k], buf + d.lds - lane * 16);
         } else if (k < XK + SK) {
             const DmaPiece d = scan_flat_piece(k - XK, w, lane, NW, Cfg::SP);
             if (d.on) {
                 const unsigned char *sv = reinterpret_cast<const unsigned char *>(p.b_in) +
                                           (((int64_t)b * p.nc + c) * p.H + h) * PN * (int64_t)sizeof(T);
-                dma16_buf(make_rsrc(sv, Cfg::ST), (uint32_t)(d.piece * 16), buf + Cfg::O_ST + d.lds - lane * 16);
+                const int src = PS == 1 ? d.piece : scan_state_src_piece(d.piece, half, PT, Cfg::PTH, Cfg::TP);
+                dma16_buf(make_rsrc(sv, Cfg::STH), (uint32_t)(src * 16), buf + Cfg::O_ST + d.lds - lane * 16);
             }
         } else {
             const int64_t tok = (((int64_t)b * p.H + h) * p.nc + c) * Q;
@@ -293,19 +299,19 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         const int i = (d.row < 16 ? I0 : I1) * 16 + (d.row & 15);
         yoff[k] = (uint32_t)i * (uint32_t)(HP * (int)sizeof(T)) + (uint32_t)(d.piece * 16);
     }
-    auto store_item = [&](int k, int hs, const unsigned char *ys) {
+    auto store_item = [&](int k, int hs, int half, const unsigned char *ys) {
         const DmaPiece d = scan_y_piece(k, lane, YPIECES);
         const int i = (d.row < 16 ? I0 : I1) * 16 + (d.row & 15);
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + d.lds);
         // y is written once and not read again in this step: non-temporal.  Only the last
         // chunk can be short, so full chunks skip the per-lane row check.
-        const rsrc_t r = make_rsrc(ychunk + (int64_t)hs * P, (uint32_t)(Qc - 1) * xrow + xhead);
+        const rsrc_t r = make_rsrc(ychunk + (int64_t)hs * P + half * PV, (uint32_t)(Qc - 1) * xrow + xunit);
         if (Qc == Q || i < Qc) __builtin_amdgcn_raw_buffer_store_b128(v, r, yoff[k], 0, kCachePolicyNT);
     };
 
 #pragma unroll
-    for (int k = 0; k < NDMA; ++k) dma_item(k, h0, smem);
+    for (int k = 0; k < NDMA; ++k) dma_item(k, h0, 0, smem);
 
     // ---- per workgroup: this wave's C fragments, then its causal S^T = B C^T tiles
     constexpr int NSTEP = sizeof(T) == 2 ? 2 : 1;
@@ -386,18 +392,21 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     }
 
     const float res = (p.flags & 1u) ? 1.f : 0.f;
-    for (int h = h0, it = 0; h < h1; ++h, ++it) {
+    // units (h, half): head h, channels [half PV, (half + 1) PV)
+    for (int h = h0, half = 0, it = 0; h < h1; ++it) {
+        const int hn = half + 1 < PS ? h : h + 1, halfn = half + 1 < PS ? half + 1 : 0;   // next unit
+        const int hp = half > 0 ? h : h - 1, halfp = half > 0 ? half - 1 : PS - 1;       // previous unit
         unsigned char *buf = smem + (Cfg::DB ? (it & 1) * Cfg::HEAD_BYTES : 0);
         unsigned char *nbuf = smem + (Cfg::DB ? ((it + 1) & 1) * Cfg::HEAD_BYTES : 0);
-        __builtin_amdgcn_s_waitcnt(0);        // this head's DMA (and older stores) complete
+        __builtin_amdgcn_s_waitcnt(0);        // this unit's DMA (and older stores) complete
         __builtin_amdgcn_s_barrier();         // ... for every wave; the other buffer is free
-        const bool more = h + 1 < h1;
-        // Item k: the next head's DMA (double buffer), then the previous head's staged stores.
+        const bool more = hn < h1;
+        // Item k: the next unit's DMA (double buffer), then the previous unit's staged stores.
         auto hook = [&](int k, unsigned char *nb, const unsigned char *yst) {
             if (k < NDMA) {
-                if (Cfg::DB && more) dma_item(k, h + 1, nb);
+                if (Cfg::DB && more) dma_item(k, hn, halfn, nb);
             } else if (k < NITEM) {
-                if (Cfg::YS && h > h0) store_item(k - NDMA, h - 1, yst);
+                if (Cfg::YS && it > 0) store_item(k - NDMA, hp, halfp, yst);
             }
         };
         const float dres = (p.D ? p.D[h] : 0.f) + res;
@@ -412,7 +421,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         for (int k = NHOOK; k < NITEM; ++k) hook(k, nbuf, ys);   // items the body had no room for
 
         if constexpr (Cfg::YS) {
-            // rounded outputs into this wave's staging rows; stored during the next head
+            // rounded outputs into this wave's staging rows; stored during the next unit
 #pragma unroll
             for (int ri = 0; ri < 2; ++ri)
 #pragma unroll
@@ -422,7 +431,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
                     *reinterpret_cast<F *>(ys + scan_y_stage(row, byte, YPIECES)) = frag_from_f32<T>(acc[ri][pt]);
                 }
         } else {
-            T *yh = ychunk + h * P;
+            T *yh = ychunk + h * P + half * PV;
 #pragma unroll
             for (int ri = 0; ri < 2; ++ri) {
                 const int i = (ri ? I1 : I0) * 16 + col;
@@ -437,12 +446,14 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
 #pragma unroll
-            for (int k = 0; k < NDMA; ++k) dma_item(k, h + 1, smem);
+            for (int k = 0; k < NDMA; ++k) dma_item(k, hn, halfn, smem);
         }
+        h = hn;
+        half = halfn;
     }
-    if constexpr (Cfg::YS) {                  // last head's staged outputs (own rows: no barrier)
+    if constexpr (Cfg::YS) {                  // last unit's staged outputs (own rows: no barrier)
 #pragma unroll
-        for (int k = 0; k < NSTQ; ++k) store_item(k, h1 - 1, ys);
+        for (int k = 0; k < NSTQ; ++k) store_item(k, h1 - 1, PS - 1, ys);
     }
 }
 

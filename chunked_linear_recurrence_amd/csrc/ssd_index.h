@@ -20,16 +20,27 @@ struct ScanCfg {
     static constexpr int NRB = Q / 16, NW = NRB / 2, THREADS = NW * 64;
     static constexpr int NSLOT = NRB + 2, NPAIR = NSLOT / 2;
     static constexpr int NTRI = NRB * (NRB + 1) / 2;            // causal tiles per chunk
-    static constexpr int PT = P / 16, NT = N / 16;
-    // one head's inputs in LDS (HeadBuf): x tile [Q][P], b(c-1) tile [P*N], the prefix
-    // sums cum [Q] and the block decays dblk [Q] (float32)
-    static constexpr int X = Q * P * E, ST = P * N * E, CM = Q * (int)sizeof(S), DL = Q * 4;
+    // A head whose inputs do not fit in LDS twice (P = 128; fp32 at Q = 256) is taken as
+    // PS = 2 units of PV = P/2 channels: a unit is a head of PV channels for the products,
+    // the LDS layout and the stores, reading its channels' slice of x, b(c-1) and y.
+    static constexpr int CM = Q * (int)sizeof(S), DL = Q * 4;
+    static constexpr int HEAD_BYTES_P = Q * P * E + P * N * E + CM + DL;
+    static constexpr int PS = (2 * HEAD_BYTES_P > kLdsBytes && (P / 2) % 16 == 0 && (P / 2) * E >= 32) ? 2 : 1;
+    static constexpr int PV = P / PS;                           // channels per unit
+    static constexpr int PT = PV / 16, NT = N / 16;             // p tiles per unit, n tiles
+    static constexpr int PTH = P / 16;                          // p tiles of a whole head
+    static constexpr int TP = 16 * E;                           // 16-byte pieces per 16x16 state tile
+    static constexpr int STH = P * N * E;                       // a head's b(c-1) in bytes
+    // one unit's inputs in LDS (HeadBuf): x tile [Q][PV], b(c-1) tile [PV*N] (the unit's p
+    // tiles of every n tile, tile order), the prefix sums cum [Q] and the block decays
+    // dblk [Q] (float32)
+    static constexpr int X = Q * PV * E, ST = PV * N * E;
     static constexpr int O_ST = X, O_CM = X + ST, O_DL = O_CM + CM;
     static constexpr int HEAD_BYTES = O_DL + DL;
     static constexpr bool DB = 2 * HEAD_BYTES <= kLdsBytes;     // double-buffered head data
-    static constexpr int XPIECES = P * E / 16;                  // 16-byte pieces per x row
-    static constexpr int YPIECES = P * E / 16;                  // 16-byte pieces per output row
-    static constexpr int YW = 32 * P * E;                       // one wave's staged outputs
+    static constexpr int XPIECES = PV * E / 16;                 // 16-byte pieces per x row
+    static constexpr int YPIECES = PV * E / 16;                 // 16-byte pieces per output row
+    static constexpr int YW = 32 * PV * E;                      // one wave's staged outputs
     static constexpr bool YS = DB && 2 * HEAD_BYTES + NW * YW <= kLdsBytes;
     static constexpr int LDS = (DB ? 2 * HEAD_BYTES : HEAD_BYTES) + (YS ? NW * YW : 0);
     // The chunk's B tile (Q x N) is staged in LDS for the S^T products when it fits beside
@@ -45,8 +56,15 @@ struct ScanCfg {
     static constexpr int NSTQ = 32 * YPIECES / 64;                    // staged-output stores
     static constexpr bool OK = LDS <= kLdsBytes &&
                                (sizeof(T) == 4 || NT % 2 == 0) && (Q == 32 || Q == 64 || Q == 128 || Q == 256) &&
-                               P * E >= 32 && CP <= THREADS && DP <= THREADS;
+                               PV * E >= 32 && CP <= THREADS && DP <= THREADS;
 };
+
+// Piece v of a unit's b(c-1) tile in LDS (its p tiles of every n tile, in tile order) as a
+// piece of the head's whole state (tile order [n tile][p tile], PTH p tiles): unit `half`
+// takes p tiles [half PT, (half + 1) PT).  The identity for a single unit (PT = PTH).
+__host__ __device__ constexpr int scan_state_src_piece(int v, int half, int PT, int PTH, int TP) {
+    return (((v / TP) / PT) * PTH + half * PT + (v / TP) % PT) * TP + v % TP;
+}
 
 // Every (Q, P, N) compiled for chunk_scan, for each activation type T (X(T, Q, P, N)).
 #define SSD_SCAN_SHAPES(X, T)                                                              \

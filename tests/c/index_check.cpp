@@ -109,10 +109,10 @@ static void check_scan_shape() {
             CHECK(xsrc[i] == 1, "%s x: source piece %d copied %d times", shape, i, xsrc[i]);
             CHECK(xdst[i] == 1, "%s x: LDS slot %d written %d times", shape, i, xdst[i]);
         }
-        if (sizeof(T) == 2) check_frag_reads("x", shape, Q, P, Cfg::NRB, Cfg::PT, Cfg::X);
-        // within one head's slice of a chunk of Qc rows: the last byte read (row Qc - 1 after
+        if (sizeof(T) == 2) check_frag_reads("x", shape, Q, Cfg::PV, Cfg::NRB, Cfg::PT, Cfg::X);
+        // within one unit's slice of a chunk of Qc rows: the last byte read (row Qc - 1 after
         // the kernel's clamp) is inside the buffer bound the kernel gives that slice,
-        // (Qc - 1) * row_pitch + P * E, for the tightest row pitch H * P = P
+        // (Qc - 1) * row_pitch + PV * E, for the tightest row pitch H * P = P
         for (int Qc : {1, Q / 2 + 3, Q}) {
             if (Qc > Q) continue;
             const long pitch = (long)P * E;
@@ -122,22 +122,35 @@ static void check_scan_shape() {
                         const DmaPiece d = scan_x_piece(k, w, lane, NW, Q, Cfg::XPIECES, sizeof(T) == 2);
                         if (!d.on) continue;
                         const long rr = d.row < Qc - 1 ? d.row : Qc - 1;
-                        CHECK(rr * pitch + d.piece * 16 + 16 <= (long)(Qc - 1) * pitch + P * E,
+                        CHECK(rr * pitch + d.piece * 16 + 16 <= (long)(Qc - 1) * pitch + Cfg::PV * E,
                               "%s x: read past the chunk (Qc %d)", shape, Qc);
                     }
         }
-        // b(c-1) tile: flat, whole waves
-        std::vector<int> sseen(Cfg::SP, 0);
-        for (int w = 0; w < NW; ++w)
-            for (int lane = 0; lane < 64; ++lane)
-                for (int kk = 0; kk < Cfg::SK; ++kk) {
-                    const DmaPiece d = scan_flat_piece(kk, w, lane, NW, Cfg::SP);
-                    if (!d.on) continue;
-                    CHECK(d.piece * 16 + 16 <= Cfg::ST, "%s b_in: piece %d", shape, d.piece);
-                    CHECK(Cfg::O_ST + d.lds + 16 <= Cfg::O_CM, "%s b_in: LDS byte %d", shape, d.lds);
-                    if (d.piece < Cfg::SP) ++sseen[d.piece];
-                }
-        for (int i = 0; i < Cfg::SP; ++i) CHECK(sseen[i] == 1, "%s b_in: piece %d copied %d times", shape, i, sseen[i]);
+        // b(c-1) tile: flat, whole waves; over a head's units, every piece of the head's
+        // state once, and each unit's LDS tile holds its p tiles of every n tile in order
+        CHECK(Cfg::PS * Cfg::PV == P && Cfg::PS * Cfg::ST == Cfg::STH && Cfg::TP * 16 == 256 * E,
+              "%s: channel units", shape);
+        std::vector<int> sseen(Cfg::STH / 16, 0);
+        for (int half = 0; half < Cfg::PS; ++half)
+            for (int w = 0; w < NW; ++w)
+                for (int lane = 0; lane < 64; ++lane)
+                    for (int kk = 0; kk < Cfg::SK; ++kk) {
+                        const DmaPiece d = scan_flat_piece(kk, w, lane, NW, Cfg::SP);
+                        if (!d.on) continue;
+                        const int src = scan_state_src_piece(d.piece, half, Cfg::PT, Cfg::PTH, Cfg::TP);
+                        CHECK(d.piece * 16 + 16 <= Cfg::ST, "%s b_in: piece %d", shape, d.piece);
+                        CHECK(src >= 0 && src * 16 + 16 <= Cfg::STH, "%s b_in: source piece %d", shape, src);
+                        CHECK(Cfg::O_ST + d.lds + 16 <= Cfg::O_CM, "%s b_in: LDS byte %d", shape, d.lds);
+                        // the source tile is (n tile, p tile) = (t / PTH, t % PTH); the LDS tile
+                        // the unit's fragment reads index as (nt, pt) = (v / PT, v % PT)
+                        const int vt = d.piece / Cfg::TP, st = src / Cfg::TP;
+                        CHECK(st / Cfg::PTH == vt / Cfg::PT && st % Cfg::PTH == half * Cfg::PT + vt % Cfg::PT &&
+                                  src % Cfg::TP == d.piece % Cfg::TP,
+                              "%s b_in: tile of piece %d", shape, d.piece);
+                        if (src >= 0 && src * 16 + 16 <= Cfg::STH) ++sseen[src];
+                    }
+        for (int i = 0; i < Cfg::STH / 16; ++i)
+            CHECK(sseen[i] == 1, "%s b_in: piece %d copied %d times", shape, i, sseen[i]);
         // cum (waves from 0 up) and dblk (waves from NW - 1 down) rows
         check_row("cum", scan_row_piece, NW, false, Cfg::CP, Cfg::O_DL - Cfg::O_CM, Cfg::CM, shape);
         check_row("dblk", scan_row_piece, NW, true, Cfg::DP, Cfg::HEAD_BYTES - Cfg::O_DL, Cfg::DL, shape);
@@ -179,7 +192,7 @@ static void check_scan_shape() {
                 CHECK(yseen[i] == 1, "%s y: staged piece %d stored %d times", shape, i, yseen[i]);
             // every fragment store (row, 4 channels at byte offset) lands inside the area
             for (int row = 0; row < 32; ++row)
-                for (int byte = 0; byte < P * E; byte += 4 * E)
+                for (int byte = 0; byte < Cfg::PV * E; byte += 4 * E)
                     CHECK(scan_y_stage(row, byte, Cfg::YPIECES) + 4 * E <= Cfg::YW, "%s y: stage row %d byte %d", shape,
                           row, byte);
         }
