@@ -92,7 +92,7 @@ def _check(status):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()      # ctypes passes ints as void *
 
 
 def _stream(stream):
@@ -114,9 +114,16 @@ def _expect(name, t, shape, dtypes, allow_none=False):
         raise ValueError("%s is required" % name)
     if not isinstance(t, torch.Tensor):
         raise ValueError("%s must be a torch.Tensor (got %s)" % (name, type(t).__name__))
-    if t.dim() != len(shape) or any(s is not None and s != d for s, d in zip(shape, t.shape)):
+    ts = t.shape
+    ok = len(ts) == len(shape)
+    if ok:
+        for s, d in zip(shape, ts):     # a plain loop: this runs on every call of every entry point
+            if s is not None and s != d:
+                ok = False
+                break
+    if not ok:
         raise ValueError("%s has shape %s; expected %s" % (
-            name, tuple(t.shape), tuple("*" if s is None else s for s in shape)))
+            name, tuple(ts), tuple("*" if s is None else s for s in shape)))
     if t.dtype not in dtypes:
         raise ValueError("%s has dtype %s; expected %s" % (
             name, t.dtype, " or ".join(str(d) for d in dtypes)))
@@ -126,13 +133,18 @@ def _expect(name, t, shape, dtypes, allow_none=False):
 
 def _same_device(**tensors):
     """All tensors on one CUDA device (checked after shapes and dtypes)."""
-    devs = {n: t.device for n, t in tensors.items() if t is not None}
-    for n, d in devs.items():
+    first = None
+    for n, t in tensors.items():
+        if t is None:
+            continue
+        d = t.device
         if d.type != "cuda":
             raise ValueError("%s is on %s; every tensor must be on a CUDA device" % (n, d))
-    if len(set(devs.values())) > 1:
-        raise ValueError("tensors are on different devices: %s" % (
-            ", ".join("%s %s" % (n, d) for n, d in devs.items())))
+        if first is None:
+            first = d
+        elif d != first:
+            raise ValueError("tensors are on different devices: %s" % (
+                ", ".join("%s %s" % (m, u.device) for m, u in tensors.items() if u is not None)))
 
 
 def check_layer_args(x, dt, A, B, C, D=None, init_state=None, y=None, final_state=None, workspace=None):
