@@ -46,12 +46,13 @@ __device__ __forceinline__ float4 fma4(float a, const float4 &s, const float4 &b
     return make_float4(fmaf(a, s.x, b.x), fmaf(a, s.y, b.y), fmaf(a, s.z, b.z), fmaf(a, s.w, b.w));
 }
 
-template <typename T>
+// One wave per 256-element group of a (batch, head) state; loads run two groups of K
+// chunks ahead of the dependent multiply-adds.
+template <typename T, int K>
 __global__ __launch_bounds__(64) void state_pass_kernel(Problem p0) {
     const Problem p = step_problem(p0, blockIdx.z / p0.batch);
     typedef typename TF<T>::type V;
     typedef typename CumT<T>::type S;
-    constexpr int K = sizeof(T) == 2 ? 16 : 8;         // chunks per load group
     const int PN = p.P * p.N;
     const int e4 = blockIdx.x * 64 + threadIdx.x;        // 4-element group within one state
     const int h = blockIdx.y, b = blockIdx.z % p0.batch;
@@ -97,11 +98,94 @@ __global__ __launch_bounds__(64) void state_pass_kernel(Problem p0) {
     if (p.final_state) *reinterpret_cast<float4 *>(p.final_state + std_off) = s;
 }
 
+// Short chains (at most KS chunks, the whole chain in one load phase): EPT groups of 256
+// elements per wave, so that a wave has enough loads in flight to cover its own start-up.
+// Each chunk's state is a uniform base plus a 32-bit per-lane offset.
+template <typename T, int KS, int EPT>
+__global__ __launch_bounds__(64) void state_pass_short_kernel(Problem p0) {
+    const Problem p = step_problem(p0, blockIdx.z / p0.batch);
+    typedef typename TF<T>::type V;
+    typedef typename CumT<T>::type S;
+    const int PN = p.P * p.N;
+    const int h = blockIdx.y, b = blockIdx.z % p0.batch;
+    const int nc = p.nc;
+    const int64_t cbytes = (int64_t)p.H * PN * (int64_t)sizeof(T);    // between chunks
+    const int64_t hbase = (((int64_t)b * p.nc * p.H + h) * PN) * (int64_t)sizeof(T);
+    const unsigned char *bi = reinterpret_cast<const unsigned char *>(p.b_intra) + hbase;
+    unsigned char *bo = reinterpret_cast<unsigned char *>(p.b_in) + hbase;
+    const S *tot = reinterpret_cast<const S *>(p.ctot) + ((int64_t)b * p.H + h) * p.nc;
+
+    uint32_t voff[EPT];
+    bool on[EPT];
+    float4 s[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int e = ((blockIdx.x * EPT + j) * 64 + threadIdx.x) * 4;
+        on[j] = e < PN;                                      // uniform: PN is a multiple of 256
+        voff[j] = (uint32_t)(on[j] ? e : 0) * (uint32_t)sizeof(T);
+        s[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    V v[KS][EPT];
+#pragma unroll
+    for (int u = 0; u < KS; ++u)
+        if (u < nc) {                                        // uniform
+            const unsigned char *src = bi + u * cbytes;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j)
+                if (on[j]) v[u][j] = __builtin_nontemporal_load(reinterpret_cast<const V *>(src + voff[j]));
+        }
+    if (p.init) {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            if (on[j]) {
+                const StateIdx pn = tile_elem((int)(voff[j] / sizeof(T)), p.P);
+                s[j] = *reinterpret_cast<const float4 *>(p.init + (((int64_t)b * p.H + h) * p.P + pn.p) * p.N + pn.n0);
+            }
+    }
+#pragma unroll
+    for (int u = 0; u < KS; ++u)
+        if (u < nc) {
+            const float a = exp2_fast((float)tot[u]);
+            unsigned char *dst = bo + u * cbytes;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j)
+                if (on[j]) {
+                    store_state<T>(reinterpret_cast<T *>(dst + voff[j]), s[j]);
+                    s[j] = fma4(a, s[j], as_float4(v[u][j]));
+                }
+        }
+    if (p.final_state) {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            if (on[j]) {
+                const StateIdx pn = tile_elem((int)(voff[j] / sizeof(T)), p.P);
+                *reinterpret_cast<float4 *>(p.final_state + (((int64_t)b * p.H + h) * p.P + pn.p) * p.N + pn.n0) = s[j];
+            }
+    }
+}
+
+template <typename T, int KS, int EPT>
+static void launch_short(const Problem &p, hipStream_t s) {
+    const int PN = p.P * p.N;
+    dim3 grid((PN / 4 + 64 * EPT - 1) / (64 * EPT), p.H, p.batch * step_count(p));
+    state_pass_short_kernel<T, KS, EPT><<<grid, 64, 0, s>>>(p);
+}
+
 hipError_t launch_state_pass(const Problem &p, hipStream_t s) {
     const int PN = p.P * p.N;
-    dim3 grid((PN / 4 + 63) / 64, p.H, p.batch * step_count(p));
-    if (p.dtype == 1) state_pass_kernel<bf16><<<grid, 64, 0, s>>>(p);
-    else state_pass_kernel<float><<<grid, 64, 0, s>>>(p);
+    const int z = p.batch * step_count(p);
+    // chains of at most 8 chunks: 4 element groups per wave; at most 16: 2
+    if (p.nc <= 8) {
+        if (p.dtype == 1) launch_short<bf16, 8, 4>(p, s);
+        else launch_short<float, 8, 4>(p, s);
+    } else if (p.nc <= 16) {
+        if (p.dtype == 1) launch_short<bf16, 16, 2>(p, s);
+        else launch_short<float, 16, 2>(p, s);
+    } else {
+        dim3 grid((PN / 4 + 63) / 64, p.H, z);
+        if (p.dtype == 1) state_pass_kernel<bf16, 16><<<grid, 64, 0, s>>>(p);
+        else state_pass_kernel<float, 8><<<grid, 64, 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 
