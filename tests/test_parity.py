@@ -163,6 +163,21 @@ def test_random_shapes(case):
     assert err(fin, fr) <= tol_for(dtype)
 
 
+@pytest.mark.parametrize("nc", [7, 8, 9, 16, 17])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_pass_chain_lengths(nc, dtype):
+    """Chains on both sides of the state pass's short-chain kernels (at most 8 and at most
+    16 chunks, several element groups per wave) and of its streaming kernel beyond, with a
+    ragged last chunk and a nonzero initial state: y and final_state against the oracle."""
+    Q, P, N = 64, 32, 64
+    d = small(2, (nc - 1) * Q + 5, 3, P, N, 1, dtype, seed=300 + nc, init=True)
+    y, fin = run_gpu(d, Q)
+    yr, fr = oracle_layer(d)
+    err = err_for(dtype)
+    assert err(y, yr) <= tol_for(dtype), (dtype, nc)
+    assert err(fin, fr) <= tol_for(dtype), (dtype, nc)
+
+
 # ------------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("L", [1, 17, 64, 65, 255, 256, 257])
