@@ -15,7 +15,10 @@
 // (K loads of the next group are in flight while the current group is consumed); the pass
 // is a pure HBM stream (read and write act bytes per state element per chunk); b_intra is
 // read with the non-temporal policy (used once), b_in is stored normally (chunk_scan reads
-// it next, and keeping its stores cacheable measured faster than streaming them).
+// it next, and keeping its stores cacheable measured faster than streaming them).  Short
+// chains (at most 16 chunks: a segment of the layer stack, a 4K-token sequence) are loaded
+// whole at once by a second kernel whose waves own 2 or 4 element groups each, so every
+// wave has enough loads in flight to cover its own start-up.
 //
 // b_intra and b_in use the tile order of the other kernels (see libssdscan.h); only
 // init_state / final_state use the row-major [P][N] order, so the thread owning tile
