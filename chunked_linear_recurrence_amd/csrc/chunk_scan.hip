@@ -211,7 +211,7 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     // b_in pieces, one cum row, one dblk row, then NSTQ staged-output stores
     constexpr int XK = Cfg::XK, SK = Cfg::SK, NDMA = Cfg::NDMA, NSTQ = Cfg::NSTQ;
     constexpr int NHOOK = 1 + PT + Cfg::NPAIR;
-    constexpr int NITEM = NDMA + (Cfg::YS ? NSTQ : 0);
+    constexpr int NITEM = NDMA + (Cfg::STAGED ? NSTQ : 0);
     static_assert(NSTQ * 64 == 32 * YPIECES, "output rows must fill whole store instructions");
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -295,12 +295,12 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     uint32_t yoff[NSTQ];
 #pragma unroll
     for (int k = 0; k < NSTQ; ++k) {
-        const DmaPiece d = scan_y_piece(k, lane, YPIECES);
+        const DmaPiece d = scan_y_piece(k, lane, YPIECES, Cfg::IP, w, NW);
         const int i = (d.row < 16 ? I0 : I1) * 16 + (d.row & 15);
         yoff[k] = (uint32_t)i * (uint32_t)(HP * (int)sizeof(T)) + (uint32_t)(d.piece * 16);
     }
     auto store_item = [&](int k, int hs, int half, const unsigned char *ys) {
-        const DmaPiece d = scan_y_piece(k, lane, YPIECES);
+        const DmaPiece d = scan_y_piece(k, lane, YPIECES, Cfg::IP, w, NW);
         const int i = (d.row < 16 ? I0 : I1) * 16 + (d.row & 15);
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + d.lds);
@@ -392,6 +392,22 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     }
 
     const float res = (p.flags & 1u) ? 1.f : 0.f;
+    // In-place staging (Cfg::IP): a unit's rounded outputs wait in registers until the top
+    // of the next unit, when every wave is past the finished buffer; each wave then writes
+    // them into its own x slots there, stores them, and only then copies the unit after
+    // next into that buffer (after its own reads of the staged rows: lgkmcnt(0)).
+    F yres[2][PT];
+    auto stage = [&](unsigned char *area) {
+#pragma unroll
+        for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const int row = ri * 16 + col;
+                const int byte = (pt * 16 + g4) * (int)sizeof(T);
+                *reinterpret_cast<F *>(area + scan_y_stage(row, byte, YPIECES, true, w, NW)) = yres[ri][pt];
+            }
+    };
+    constexpr int kWaitLds = 0xC07F;          // s_waitcnt lgkmcnt(0) alone (vmcnt 63, expcnt 7)
     // units (h, half): head h, channels [half PV, (half + 1) PV)
     for (int h = h0, half = 0, it = 0; h < h1; ++it) {
         const int hn = half + 1 < PS ? h : h + 1, halfn = half + 1 < PS ? half + 1 : 0;   // next unit
@@ -401,12 +417,27 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
         __builtin_amdgcn_s_waitcnt(0);        // this unit's DMA (and older stores) complete
         __builtin_amdgcn_s_barrier();         // ... for every wave; the other buffer is free
         const bool more = hn < h1;
-        // Item k: the next unit's DMA (double buffer), then the previous unit's staged stores.
+        if constexpr (Cfg::IP) {
+            if (it > 0) stage(nbuf);          // the previous unit's outputs, into its own buffer
+        }
+        // Item k: the next unit's DMA (double buffer), then the previous unit's staged stores;
+        // staged in place, the stores come first.
         auto hook = [&](int k, unsigned char *nb, const unsigned char *yst) {
-            if (k < NDMA) {
-                if (Cfg::DB && more) dma_item(k, hn, halfn, nb);
-            } else if (k < NITEM) {
-                if (Cfg::YS && it > 0) store_item(k - NDMA, hp, halfp, yst);
+            if constexpr (Cfg::IP) {
+                if (k < NSTQ) {
+                    if (it > 0) store_item(k, hp, halfp, nb);
+                } else if (k < NITEM) {
+                    if (more) {
+                        if (k == NSTQ && it > 0) __builtin_amdgcn_s_waitcnt(kWaitLds);
+                        dma_item(k - NSTQ, hn, halfn, nb);
+                    }
+                }
+            } else {
+                if (k < NDMA) {
+                    if (Cfg::DB && more) dma_item(k, hn, halfn, nb);
+                } else if (k < NITEM) {
+                    if (Cfg::YS && it > 0) store_item(k - NDMA, hp, halfp, yst);
+                }
             }
         };
         const float dres = (p.D ? p.D[h] : 0.f) + res;
@@ -430,6 +461,11 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
                     const int byte = (pt * 16 + g4) * (int)sizeof(T);
                     *reinterpret_cast<F *>(ys + scan_y_stage(row, byte, YPIECES)) = frag_from_f32<T>(acc[ri][pt]);
                 }
+        } else if constexpr (Cfg::IP) {
+#pragma unroll
+            for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) yres[ri][pt] = frag_from_f32<T>(acc[ri][pt]);
         } else {
             T *yh = ychunk + h * P + half * PV;
 #pragma unroll
@@ -454,6 +490,14 @@ __global__ __launch_bounds__((ScanCfg<T, Q, P, N>::THREADS)) void chunk_scan_ker
     if constexpr (Cfg::YS) {                  // last unit's staged outputs (own rows: no barrier)
 #pragma unroll
         for (int k = 0; k < NSTQ; ++k) store_item(k, h1 - 1, PS - 1, ys);
+    }
+    if constexpr (Cfg::IP) {                  // last unit: staged once every wave is past its x
+        unsigned char *last = smem + (((h1 - h0) * PS - 1) & 1) * Cfg::HEAD_BYTES;
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        stage(last);
+#pragma unroll
+        for (int k = 0; k < NSTQ; ++k) store_item(k, h1 - 1, PS - 1, last);
     }
 }
 

@@ -41,7 +41,13 @@ struct ScanCfg {
     static constexpr int XPIECES = PV * E / 16;                 // 16-byte pieces per x row
     static constexpr int YPIECES = PV * E / 16;                 // 16-byte pieces per output row
     static constexpr int YW = 32 * PV * E;                      // one wave's staged outputs
+    // Outputs leave through LDS rows (whole 128-byte output rows per store): a separate
+    // staging area when it fits beside the two head buffers (YS), else in place (IP): each
+    // wave stages its rows in its own x slots of the finished head buffer (a wave's 32
+    // output rows are exactly as many bytes as its share of the x copy).
     static constexpr bool YS = DB && 2 * HEAD_BYTES + NW * YW <= kLdsBytes;
+    static constexpr bool IP = DB && !YS;
+    static constexpr bool STAGED = YS || IP;
     static constexpr int LDS = (DB ? 2 * HEAD_BYTES : HEAD_BYTES) + (YS ? NW * YW : 0);
     // The chunk's B tile (Q x N) is staged in LDS for the S^T products when it fits beside
     // the first head's buffer; otherwise the B fragments are loaded from L2.
@@ -145,19 +151,30 @@ __host__ __device__ constexpr DmaPiece scan_b_piece(int k, int w, int lane, int 
 // spread over all banks.
 __host__ __device__ constexpr int ysw(int r, int ypieces) { return r & ((ypieces < 8 ? ypieces : 8) - 1); }
 
+// Start of staged row r of wave w.  In a separate staging area (inplace false) the wave's
+// rows are contiguous (offsets inside the wave's area).  In place, the rows fill the
+// wave's own 1 KB x-copy slots of a head buffer, slots k * NW + w for k = 0..XK-1,
+// 64 / ypieces rows per slot (offsets inside the buffer).
+__host__ __device__ constexpr int scan_y_row_base(int row, int ypieces, bool inplace, int w, int NW) {
+    return inplace ? ((row / (64 / ypieces)) * NW + w) * 1024 + (row % (64 / ypieces)) * ypieces * 16
+                   : row * ypieces * 16;
+}
+
 // Store item k (< NSTQ) of a wave's staged rows: the staging row (0..31; rows 0..15 are
 // tokens of row block I0, 16..31 of I1), the 16-byte piece of the output row, and the LDS
 // byte offset it is read from.
-__host__ __device__ constexpr DmaPiece scan_y_piece(int k, int lane, int ypieces) {
+__host__ __device__ constexpr DmaPiece scan_y_piece(int k, int lane, int ypieces, bool inplace = false, int w = 0,
+                                                   int NW = 1) {
     const int pc = k * 64 + lane;
     const int row = pc / ypieces, q = pc % ypieces;
-    return DmaPiece{true, row, q, (row * ypieces + (q ^ ysw(row, ypieces))) * 16};
+    return DmaPiece{true, row, q, scan_y_row_base(row, ypieces, inplace, w, NW) + (q ^ ysw(row, ypieces)) * 16};
 }
 
 // LDS byte offset of the staged output value (row, byte) written by the fragment stores:
 // row = ri * 16 + token within the block, byte = channel * sizeof(T).
-__host__ __device__ constexpr int scan_y_stage(int row, int byte, int ypieces) {
-    return (row * ypieces + ((byte >> 4) ^ ysw(row, ypieces))) * 16 + (byte & 15);
+__host__ __device__ constexpr int scan_y_stage(int row, int byte, int ypieces, bool inplace = false, int w = 0,
+                                               int NW = 1) {
+    return scan_y_row_base(row, ypieces, inplace, w, NW) + ((byte >> 4) ^ ysw(row, ypieces)) * 16 + (byte & 15);
 }
 
 // ---------------------------------------------------------------------------------

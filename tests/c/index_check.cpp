@@ -174,27 +174,44 @@ static void check_scan_shape() {
                 CHECK(bseen[i] == 1, "%s B: piece %d copied %d times", shape, i, bseen[i]);
         }
         // staged outputs: each (row, piece) read exactly once, from where the fragment
-        // stores put it, inside the wave's staging area
-        if (Cfg::YS) {
-            std::vector<int> yseen(32 * Cfg::YPIECES, 0);
-            for (int k = 0; k < Cfg::NSTQ; ++k)
-                for (int lane = 0; lane < 64; ++lane) {
-                    const DmaPiece d = scan_y_piece(k, lane, Cfg::YPIECES);
-                    CHECK(d.row >= 0 && d.row < 32 && d.piece >= 0 && d.piece < Cfg::YPIECES, "%s y: row %d piece %d",
-                          shape, d.row, d.piece);
-                    CHECK(d.lds >= 0 && d.lds + 16 <= Cfg::YW, "%s y: LDS byte %d", shape, d.lds);
-                    CHECK(d.lds == scan_y_stage(d.row, d.piece * 16, Cfg::YPIECES), "%s y: row %d piece %d misplaced",
-                          shape, d.row, d.piece);
-                    if (d.row >= 0 && d.row < 32 && d.piece >= 0 && d.piece < Cfg::YPIECES)
-                        ++yseen[d.row * Cfg::YPIECES + d.piece];
-                }
-            for (int i = 0; i < 32 * Cfg::YPIECES; ++i)
-                CHECK(yseen[i] == 1, "%s y: staged piece %d stored %d times", shape, i, yseen[i]);
-            // every fragment store (row, 4 channels at byte offset) lands inside the area
-            for (int row = 0; row < 32; ++row)
-                for (int byte = 0; byte < Cfg::PV * E; byte += 4 * E)
-                    CHECK(scan_y_stage(row, byte, Cfg::YPIECES) + 4 * E <= Cfg::YW, "%s y: stage row %d byte %d", shape,
-                          row, byte);
+        // stores put it: in the wave's staging area (YS), or in place (IP), inside the
+        // wave's own x-copy slots of a head buffer, which no other wave writes
+        if (Cfg::STAGED) {
+            CHECK(Cfg::IP != Cfg::YS, "%s y: one staging mode", shape);
+            for (int w = 0; w < (Cfg::IP ? NW : 1); ++w) {
+                // bytes of the area this wave may stage into
+                auto own = [&](int byte) {
+                    if (!Cfg::IP) return byte >= 0 && byte < Cfg::YW;
+                    if (byte < 0 || byte >= Cfg::X) return false;
+                    const int slot = byte / 1024;       // x item k of wave w fills slot k * NW + w
+                    return slot % NW == w && slot / NW < Cfg::XK;
+                };
+                std::vector<int> yseen(32 * Cfg::YPIECES, 0);
+                std::vector<int> at(Cfg::IP ? Cfg::X : Cfg::YW, 0);
+                for (int k = 0; k < Cfg::NSTQ; ++k)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const DmaPiece d = scan_y_piece(k, lane, Cfg::YPIECES, Cfg::IP, w, NW);
+                        CHECK(d.row >= 0 && d.row < 32 && d.piece >= 0 && d.piece < Cfg::YPIECES,
+                              "%s y: row %d piece %d", shape, d.row, d.piece);
+                        CHECK(own(d.lds) && own(d.lds + 15), "%s y: wave %d reads LDS byte %d", shape, w, d.lds);
+                        CHECK(d.lds == scan_y_stage(d.row, d.piece * 16, Cfg::YPIECES, Cfg::IP, w, NW),
+                              "%s y: row %d piece %d misplaced", shape, d.row, d.piece);
+                        if (d.row >= 0 && d.row < 32 && d.piece >= 0 && d.piece < Cfg::YPIECES)
+                            ++yseen[d.row * Cfg::YPIECES + d.piece];
+                    }
+                for (int i = 0; i < 32 * Cfg::YPIECES; ++i)
+                    CHECK(yseen[i] == 1, "%s y: staged piece %d stored %d times", shape, i, yseen[i]);
+                // every fragment store (row, 4 channels at byte offset) lands inside the area,
+                // and no two overlap
+                for (int row = 0; row < 32; ++row)
+                    for (int byte = 0; byte < Cfg::PV * E; byte += 4 * E) {
+                        const int o = scan_y_stage(row, byte, Cfg::YPIECES, Cfg::IP, w, NW);
+                        const bool in = own(o) && own(o + 4 * E - 1);
+                        CHECK(in, "%s y: wave %d stage row %d byte %d at %d", shape, w, row, byte, o);
+                        if (in)
+                            for (int e = 0; e < 4 * E; ++e) CHECK(++at[o + e] == 1, "%s y: byte %d staged twice", shape, o + e);
+                    }
+            }
         }
     }
 }
