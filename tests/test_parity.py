@@ -271,6 +271,32 @@ def test_head_grouping_does_not_change_the_result(monkeypatch):
     assert err_bf16(outs[0][0], yr) <= 2e-2
 
 
+@pytest.mark.parametrize("dtype,Q,P,N", [
+    ("bf16", 256, 64, 128),      # separate staging rows (the tuned shape)
+    ("bf16", 256, 64, 256),      # outputs staged in place
+    ("f32", 128, 64, 128),       # outputs staged in place
+    ("bf16", 256, 128, 128),     # each head as two channel units
+    ("f32", 256, 64, 64),        # each head as two channel units
+])
+def test_staging_modes_over_several_heads(monkeypatch, dtype, Q, P, N):
+    """chunk_scan's staging modes and channel units with several heads per workgroup (the
+    outputs of one head are staged and stored while the next is computed): against the
+    oracle, and bit-identical to one head per workgroup."""
+    code = 0 if dtype == "f32" else 1
+    if not ssd.shape_supported(code, Q, P, N):
+        pytest.skip("shape not compiled")
+    d = small(2, 2 * Q + 37, 6, P, N, 2, dtype, seed=Q + P + N)
+    outs = []
+    for hc in ("1", "3"):
+        monkeypatch.setenv("SSD_HEADS_PER_WG_SCAN", hc)
+        outs.append(run_gpu(d, Q))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    yr, fr = oracle_layer(d)
+    err = err_for(dtype)
+    assert err(outs[1][0], yr) <= tol_for(dtype), (dtype, Q, P, N)
+    assert err(outs[1][1], fr) <= tol_for(dtype), (dtype, Q, P, N)
+
+
 def _compiled_shapes():
     try:
         return [(dt, Q, P, N) for dt in (0, 1) for Q in (32, 64, 128, 256) for P in (16, 32, 64, 128)
