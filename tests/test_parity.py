@@ -279,9 +279,9 @@ def test_head_grouping_does_not_change_the_result(monkeypatch):
     ("f32", 256, 64, 64),        # each head as two channel units
 ])
 def test_staging_modes_over_several_heads(monkeypatch, dtype, Q, P, N):
-    """chunk_scan's staging modes and channel units with several heads per workgroup (the
-    outputs of one head are staged and stored while the next is computed): against the
-    oracle, and bit-identical to one head per workgroup."""
+    """chunk_scan's staging modes and channel units, and chunk_state's wave split, with
+    several heads per workgroup (the outputs of one head are staged and stored while the
+    next is computed): against the oracle, and bit-identical to one head per workgroup."""
     code = 0 if dtype == "f32" else 1
     if not ssd.shape_supported(code, Q, P, N):
         pytest.skip("shape not compiled")
@@ -289,6 +289,7 @@ def test_staging_modes_over_several_heads(monkeypatch, dtype, Q, P, N):
     outs = []
     for hc in ("1", "3"):
         monkeypatch.setenv("SSD_HEADS_PER_WG_SCAN", hc)
+        monkeypatch.setenv("SSD_HEADS_PER_WG_STATE", hc)
         outs.append(run_gpu(d, Q))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     yr, fr = oracle_layer(d)
