@@ -65,6 +65,9 @@ def parse():
                     "(default: --steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="time only the 24-layer vertical stack in the wavefront schedule and print its "
+                         "object (for kernel traces of that schedule); not the benchmark line")
     return ap.parse_args()
 
 
@@ -134,7 +137,7 @@ def measured_traffic(workload, kernel):
     return t["kernels"][kernel]["bytes"]
 
 
-def stack_timing(torch, dev, reps=5):
+def stack_timing(torch, dev, reps=5, schedules=("wavefront", "one_at_a_time", "horizontal")):
     """The 24-layer vertical stack (32768 tokens, V = 2048): the segmented entry point in
     the wavefront schedule and one step at a time, and the horizontal order (one
     ssd_chunk_scan_fwd per layer) for reference; HIP events around `reps` whole stacks."""
@@ -161,6 +164,8 @@ def stack_timing(torch, dev, reps=5):
     out = {"workload": w.name, "layers": w.layers, "tokens": w.tokens, "V": w.segment}
     for name, f in (("wavefront", lambda: seg(True)), ("one_at_a_time", lambda: seg(False)),
                     ("horizontal", hor)):
+        if name not in schedules:
+            continue
         for _ in range(2):
             f()
         torch.cuda.synchronize()
@@ -296,6 +301,13 @@ def main():
         sys.exit(2)
     import torch
     from chunked_linear_recurrence_amd import inputs, ssd, WORKLOADS, BENCH_WORKLOAD
+
+    if args.stack_only:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        ssd.lib()
+        print(json.dumps({"stack": stack_timing(torch, dev, schedules=("wavefront",))}), flush=True)
+        return
 
     w = WORKLOADS[args.workload or BENCH_WORKLOAD]
     if w.layers > 1:
